@@ -1,0 +1,174 @@
+"""Python binding of libdllm: the per-denoising-step quantized GEMM stream of a
+diffusion LM as hand-written HIP kernels for MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in libdllm's kernels.
+PyTorch supplies device memory and the current stream.  The functions keep
+the C-ABI names without the ``dllm_`` prefix.  If libdllm.so is missing this
+module raises on import; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+Q4_K = 12
+Q6_K = 14
+Q8_K = 15
+QK_K = 256
+Q4_K_BYTES = 144
+Q6_K_BYTES = 210
+Q8_K_BYTES = 292
+DECODED_BYTES = 356
+
+E_ARG, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_HIP, E_WORKSPACE = -1, -2, -3, -4, -5, -6
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdllm.so")
+
+HEADER_EXPORTS = (
+    "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_decode_qk",
+    "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_lmhead_workspace_bytes",
+    "dllm_lmhead_masked", "dllm_qgemm_partials_i32",
+)
+
+
+class DllmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libdllm error {code}: {message}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run diffusion_lm_gemm_amd/build.py "
+                          "(or __graft_entry__.build()) first -- there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "dllm_abi_version": (I, []),
+        "dllm_last_error": (ctypes.c_char_p, []),
+        "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P]),
+        "dllm_decode_qk": (I, [I, P, I64, P, P]),
+        "dllm_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
+        "dllm_qgemm": (I, [I, P, I64, I64, P, I64, P, I64, P, I64, P]),
+        "dllm_lmhead_workspace_bytes": (I64, [I, I64, I64, I64]),
+        "dllm_lmhead_masked": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, I64, P]),
+        "dllm_qgemm_partials_i32": (I, [I, P, I64, I64, P, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.dllm_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib.dllm_abi_version()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DllmError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("libdllm takes device tensors only")
+    return t.device
+
+
+def block_bytes(qtype: int) -> int:
+    return {Q4_K: Q4_K_BYTES, Q6_K: Q6_K_BYTES}.get(qtype, 0)
+
+
+def quantize_q8k(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """f32 [M, K] (row stride = ldx) -> Q8_K records uint8 [M, K/256*292]."""
+    dev = _dev(x)
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K // QK_K * Q8_K_BYTES), dtype=torch.uint8, device=dev)
+    _check(lib.dllm_quantize_q8k(_ptr(x), M, K, x.stride(0), _ptr(out), _stream(dev)))
+    return out
+
+
+def decode_qk(qtype: int, w: torch.Tensor, n_superblocks: int,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Super-blocks -> shared decoded records uint8 [n_superblocks, 356]."""
+    dev = _dev(w)
+    if out is None:
+        out = torch.empty((n_superblocks, DECODED_BYTES), dtype=torch.uint8, device=dev)
+    _check(lib.dllm_decode_qk(qtype, _ptr(w), n_superblocks, _ptr(out), _stream(dev)))
+    return out
+
+
+def qgemm_workspace_bytes(qtype: int, N: int, K: int, M: int) -> int:
+    return int(lib.dllm_qgemm_workspace_bytes(qtype, N, K, M))
+
+
+def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: int,
+          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] (f32) = dequant(x_q8k) @ dequant(w)^T.  `y` may be a row-strided
+    view; `workspace` (uint8, >= qgemm_workspace_bytes) enables the K split."""
+    dev = _dev(w)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    assert y.dtype == torch.float32 and y.stride(1) == 1
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dllm_qgemm(qtype, _ptr(w), N, K, _ptr(x_q8k), M, _ptr(y), y.stride(0),
+                          _ptr(workspace), wsb, _stream(dev)))
+    return y
+
+
+def lmhead_workspace_bytes(qtype: int, N: int, K: int, n_rows: int) -> int:
+    return int(lib.dllm_lmhead_workspace_bytes(qtype, N, K, n_rows))
+
+
+def lmhead_masked(qtype: int, w: torch.Tensor, N: int, K: int, h: torch.Tensor,
+                  rows: torch.Tensor, logits: torch.Tensor | None = None,
+                  argmax: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """Gather rows of h, quantize to Q8_K, multiply by w: (f32 logits
+    [n_rows, N], int32 argmax [n_rows])."""
+    dev = _dev(w)
+    assert h.dtype == torch.float32 and h.stride(1) == 1 and rows.dtype == torch.int32
+    M = h.shape[0]
+    n = rows.numel()
+    if logits is None:
+        logits = torch.empty((n, N), dtype=torch.float32, device=dev)
+    if argmax is None:
+        argmax = torch.empty(n, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(lmhead_workspace_bytes(qtype, N, K, n), 1),
+                                dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib.dllm_lmhead_masked(qtype, _ptr(w), N, K, _ptr(h), M, h.stride(0), _ptr(rows), n,
+                                  _ptr(logits), logits.stride(0), _ptr(argmax), _ptr(workspace),
+                                  wsb, _stream(dev)))
+    return logits, argmax
+
+
+def qgemm_partials_i32(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor,
+                       M: int) -> torch.Tensor:
+    """Test export: int32 [M, N, K/256, 16] per-16 partial dots."""
+    dev = _dev(w)
+    P = torch.empty((M, N, K // QK_K, 16), dtype=torch.int32, device=dev)
+    _check(lib.dllm_qgemm_partials_i32(qtype, _ptr(w), N, K, _ptr(x_q8k), M, _ptr(P), _stream(dev)))
+    return P

@@ -1,0 +1,282 @@
+// libdllm C ABI: host-side argument checks, launch planning and kernel
+// launches.  Every check runs before anything is enqueued; messages follow
+// the pages' rule that errors are explicit and actionable, with no silent
+// fallback for unsupported types (technical specification, GGUF reader and
+// error-handling sections).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/dllm.h"
+#include "common.hpp"
+
+#include "kernels.hpp"
+
+using namespace dllm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return DLLM_OK;
+}
+
+const char* qname(int qtype) {
+  switch (qtype) {
+    case 0: return "F32";
+    case 1: return "F16";
+    case 2: return "Q4_0";
+    case 3: return "Q4_1";
+    case 6: return "Q5_0";
+    case 7: return "Q5_1";
+    case 8: return "Q8_0";
+    case 10: return "Q2_K";
+    case 11: return "Q3_K";
+    case 12: return "Q4_K";
+    case 13: return "Q5_K";
+    case 14: return "Q6_K";
+    case 15: return "Q8_K";
+    case 30: return "BF16";
+    default: return "unknown";
+  }
+}
+
+int check_qtype(int qtype) {
+  if (qtype != DLLM_Q4_K && qtype != DLLM_Q6_K)
+    return fail(DLLM_E_UNSUPPORTED,
+                "unsupported weight type %s (GGUF type id %d): matrix kernels exist for Q4_K and Q6_K only",
+                qname(qtype), qtype);
+  return DLLM_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
+
+int check_weights(int qtype, const void* w) {
+  const uintptr_t need = (qtype == DLLM_Q4_K) ? 16 : 4;
+  if (!aligned(w, need))
+    return fail(DLLM_E_ALIGN, "weight pointer %p must be %d-byte aligned for %s", w, (int)need, qname(qtype));
+  return DLLM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DLLM_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The GEMM kernels address weights and activations with 32-bit buffer
+// offsets: each operand (plus one tile of padding rows) must stay below 2 GiB.
+int check_buffer_sizes(const char* fn, int qtype, int64_t N, int64_t K, int64_t M) {
+  const int64_t per = (qtype == DLLM_Q4_K) ? Q4K_BYTES : Q6K_BYTES;
+  const int64_t limit = ((int64_t)1 << 31) - 1;
+  if ((N + 64) * (K / 256) * per > limit)
+    return fail(DLLM_E_SHAPE, "%s: weight matrix of %lld x %lld is larger than 2 GiB; split it by rows", fn,
+                (long long)N, (long long)K);
+  if ((M + 160) * (K / 256) * Q8K_BYTES > limit)
+    return fail(DLLM_E_SHAPE, "%s: activations of %lld x %lld are larger than 2 GiB; split them by tokens", fn,
+                (long long)M, (long long)K);
+  return DLLM_OK;
+}
+
+// Token blocks of 16 per work-group (at most 160 tokens per work-group).
+int tb_for(int64_t M) {
+  const int64_t tb = cdiv(M, 16);
+  return (int)(tb > 10 ? 10 : tb);
+}
+
+struct Plan {
+  int tb;
+  int64_t n_tiles, m_tiles;
+  int S;    // K splits
+  int sps;  // super-blocks per split
+};
+
+// K is split only when the (row tile x token tile) grid is too small to give
+// every CU two work-groups; each split keeps at least four super-blocks.
+Plan plan_gemm(int64_t N, int64_t K, int64_t M) {
+  Plan p;
+  p.tb = tb_for(M);
+  p.n_tiles = cdiv(N, 64);
+  p.m_tiles = cdiv(M, 16 * p.tb);
+  const int64_t SB = K / 256;
+  const int64_t tiles = p.n_tiles * p.m_tiles;
+  const int64_t target = 512;
+  int64_t S = (tiles >= target) ? 1 : cdiv(target, tiles);
+  const int64_t smax = SB / 4 > 0 ? SB / 4 : 1;
+  if (S > smax) S = smax;
+  if (S < 1) S = 1;
+  int64_t sps = cdiv(SB, S);
+  S = cdiv(SB, sps);
+  p.S = (int)S;
+  p.sps = (int)sps;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dllm_abi_version(void) { return DLLM_ABI_VERSION; }
+
+const char* dllm_last_error(void) { return g_err; }
+
+int dllm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, void* y_q8k, void* stream) {
+  if (!x || !y_q8k) return fail(DLLM_E_ARG, "dllm_quantize_q8k: null pointer (x=%p, y=%p)", (const void*)x, y_q8k);
+  if (M <= 0 || K <= 0 || K % 256)
+    return fail(DLLM_E_SHAPE, "dllm_quantize_q8k: need M > 0 and K a positive multiple of 256 (M=%lld, K=%lld)",
+                (long long)M, (long long)K);
+  if (ldx < K) return fail(DLLM_E_ARG, "dllm_quantize_q8k: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
+  if (!aligned(x, 4) || !aligned(y_q8k, 4)) return fail(DLLM_E_ALIGN, "dllm_quantize_q8k: x and y must be 4-byte aligned");
+  return hip_status(launch_quantize_q8k(x, ldx, nullptr, M, K / 256, (uint8_t*)y_q8k, (hipStream_t)stream),
+                    "dllm_quantize_q8k launch");
+}
+
+int dllm_decode_qk(int qtype, const void* w, int64_t n_superblocks, void* out, void* stream) {
+  int rc = check_qtype(qtype);
+  if (rc) return rc;
+  if (!w || !out) return fail(DLLM_E_ARG, "dllm_decode_qk: null pointer (w=%p, out=%p)", w, out);
+  if (n_superblocks <= 0) return fail(DLLM_E_SHAPE, "dllm_decode_qk: n_superblocks=%lld must be > 0", (long long)n_superblocks);
+  if ((rc = check_weights(qtype, w))) return rc;
+  if (!aligned(out, 4)) return fail(DLLM_E_ALIGN, "dllm_decode_qk: out must be 4-byte aligned");
+  return hip_status(launch_decode_qk(qtype, (const uint8_t*)w, n_superblocks, (uint8_t*)out, (hipStream_t)stream),
+                    "dllm_decode_qk launch");
+}
+
+int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M) {
+  if (check_qtype(qtype) || N <= 0 || M <= 0 || K <= 0 || K % 256) return -1;
+  const Plan p = plan_gemm(N, K, M);
+  return p.S > 1 ? (int64_t)p.S * M * N * 4 : 0;
+}
+
+static int check_gemm_args(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const void* xq, int64_t M) {
+  int rc = check_qtype(qtype);
+  if (rc) return rc;
+  if (!w || !xq) return fail(DLLM_E_ARG, "%s: null pointer (w=%p, x_q8k=%p)", fn, w, xq);
+  if (N <= 0 || M <= 0 || K <= 0 || K % 256)
+    return fail(DLLM_E_SHAPE, "%s: need N > 0, M > 0 and K a positive multiple of 256 (N=%lld, K=%lld, M=%lld)", fn,
+                (long long)N, (long long)K, (long long)M);
+  if (N > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "%s: N=%lld exceeds 2^31-1", fn, (long long)N);
+  if ((rc = check_weights(qtype, w))) return rc;
+  if (!aligned(xq, 4)) return fail(DLLM_E_ALIGN, "%s: x_q8k must be 4-byte aligned", fn);
+  if ((rc = check_buffer_sizes(fn, qtype, N, K, M))) return rc;
+  return DLLM_OK;
+}
+
+int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M, float* y, int64_t ldy,
+               void* workspace, int64_t workspace_bytes, void* stream) {
+  int rc = check_gemm_args("dllm_qgemm", qtype, w, N, K, x_q8k, M);
+  if (rc) return rc;
+  if (!y) return fail(DLLM_E_ARG, "dllm_qgemm: null output pointer");
+  if (ldy < N) return fail(DLLM_E_ARG, "dllm_qgemm: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
+  if (!aligned(y, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm: y must be 4-byte aligned");
+  Plan pl = plan_gemm(N, K, M);
+  const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
+  if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) {
+    pl.S = 1;  // no usable workspace: run the whole K range per work-group
+    pl.sps = (int)(K / 256);
+  }
+  GemmParams p;
+  p.w = (const uint8_t*)w;
+  p.xq = (const uint8_t*)x_q8k;
+  p.keys = nullptr;
+  p.N = N;
+  p.SB = K / 256;
+  p.M = M;
+  p.sps = pl.sps;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
+  if (pl.S == 1) {
+    p.out = y;
+    p.ldo = ldy;
+    p.split_stride = 0;
+    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, grid, false, s), "dllm_qgemm launch"))) return rc;
+    return ok();
+  }
+  p.out = (float*)workspace;
+  p.ldo = N;
+  p.split_stride = M * N;
+  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, grid, false, s), "dllm_qgemm launch"))) return rc;
+  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, s), "dllm_qgemm reduce launch");
+}
+
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_rows) {
+  if (check_qtype(qtype) || N <= 0 || K <= 0 || K % 256 || n_rows <= 0) return -1;
+  return align256(n_rows * (K / 256) * Q8K_BYTES) + cdiv(N, 64) * n_rows * 8;
+}
+
+int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
+                       const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  int rc = check_qtype(qtype);
+  if (rc) return rc;
+  if (!w || !h || !rows || !logits || !argmax || !workspace)
+    return fail(DLLM_E_ARG,
+                "dllm_lmhead_masked: null pointer (w=%p, h=%p, rows=%p, logits=%p, argmax=%p, workspace=%p)", w,
+                (const void*)h, (const void*)rows, (void*)logits, (void*)argmax, workspace);
+  if (N <= 0 || M <= 0 || K <= 0 || K % 256)
+    return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: need N > 0, M > 0, K a positive multiple of 256 (N=%lld, K=%lld, M=%lld)",
+                (long long)N, (long long)K, (long long)M);
+  if (n_rows < 1 || n_rows > M)
+    return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: n_rows=%lld must be in [1, M=%lld]", (long long)n_rows, (long long)M);
+  if (N > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: N=%lld exceeds 2^31-1", (long long)N);
+  if ((rc = check_buffer_sizes("dllm_lmhead_masked", qtype, N, K, n_rows))) return rc;
+  if (ldh < K) return fail(DLLM_E_ARG, "dllm_lmhead_masked: ldh=%lld < K=%lld", (long long)ldh, (long long)K);
+  if (ldl < N) return fail(DLLM_E_ARG, "dllm_lmhead_masked: ldl=%lld < N=%lld", (long long)ldl, (long long)N);
+  if ((rc = check_weights(qtype, w))) return rc;
+  if (!aligned(h, 4) || !aligned(logits, 4) || !aligned(rows, 4) || !aligned(argmax, 4))
+    return fail(DLLM_E_ALIGN, "dllm_lmhead_masked: h, rows, logits and argmax must be 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(DLLM_E_ALIGN, "dllm_lmhead_masked: workspace must be 256-byte aligned");
+  const int64_t need = dllm_lmhead_workspace_bytes(qtype, N, K, n_rows);
+  if (workspace_bytes < need)
+    return fail(DLLM_E_WORKSPACE, "dllm_lmhead_masked: workspace of %lld bytes, need %lld", (long long)workspace_bytes,
+                (long long)need);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t SB = K / 256;
+  uint8_t* xq = (uint8_t*)workspace;
+  uint64_t* keys = (uint64_t*)((uint8_t*)workspace + align256(n_rows * SB * Q8K_BYTES));
+  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, s), "dllm_lmhead_masked gather/quantize launch")))
+    return rc;
+  GemmParams p;
+  p.w = (const uint8_t*)w;
+  p.xq = xq;
+  p.out = logits;
+  p.keys = keys;
+  p.N = N;
+  p.SB = SB;
+  p.M = n_rows;
+  p.ldo = ldl;
+  p.split_stride = 0;
+  p.sps = (int)SB;
+  const int tb = tb_for(n_rows);
+  const int64_t n_tiles = cdiv(N, 64);
+  const dim3 grid((unsigned)n_tiles, 1, (unsigned)cdiv(n_rows, 16 * tb));
+  if ((rc = hip_status(launch_qgemm(qtype, p, tb, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
+  return hip_status(launch_argmax_finalize(keys, n_tiles, n_rows, argmax, s), "dllm_lmhead_masked argmax launch");
+}
+
+int dllm_qgemm_partials_i32(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M, int32_t* P,
+                            void* stream) {
+  int rc = check_gemm_args("dllm_qgemm_partials_i32", qtype, w, N, K, x_q8k, M);
+  if (rc) return rc;
+  if (!P) return fail(DLLM_E_ARG, "dllm_qgemm_partials_i32: null output pointer");
+  if (!aligned(P, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm_partials_i32: P must be 4-byte aligned");
+  if (M * N * (K / 256) * 16 > ((int64_t)1 << 40))
+    return fail(DLLM_E_SHAPE, "dllm_qgemm_partials_i32: output too large for a test export");
+  return hip_status(launch_partials(qtype, (const uint8_t*)w, N, K / 256, (const uint8_t*)x_q8k, M, P,
+                                    (hipStream_t)stream),
+                    "dllm_qgemm_partials_i32 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,505 @@
+// Quantized GEMM Q8_K x {Q4_K, Q6_K} on CDNA4 MFMA, with the masked-row LM
+// head's argmax epilogue.
+//
+// What is computed (mojo-dllm Development plan, "Compute design"): every
+// linear layer of a denoising step multiplies L per-token Q8_K activation rows
+// by GGUF weight rows; with x_hat = d_x q and w_hat the dequantized weights,
+//   y[m][n] = sum_sb d_x[m,sb] * sum_{i<256} w_hat[n, 256 sb + i] q[m, 256 sb + i].
+// The pages' CPU micro-kernel works on the shared form (unsigned bytes, an
+// int16 scale per 16, an f32 offset per 16).  On gfx950 the same sums are
+// arranged for the matrix cores:
+//
+//  * Integer sub-block scales are folded into the weight operand while it is
+//    unpacked in registers, as two exact int8 planes:
+//      Q4_K: sc*u = 8*(sh*u) + (sl*u), sc = 8 sh + sl, so both planes <= 105;
+//      Q6_K: s*(q-32) = 128*hi + lo, lo in [0,127], hi in [-32,32].
+//    Two v_mfma_i32_16x16x64_i8 per 64-wide K chunk give the exact int32
+//    super-block dot A_sb = (hi << shift) + lo (|A_sb| < 2^31).
+//  * The super-block epilogue in f32: y += (d * d_x) * A_sb.
+//  * Q4_K's min term -dmin * sum_j m_j * (bsum_{2j} + bsum_{2j+1}) * d_x is a
+//    K/32-long contraction; its operands (-dmin*m_j exact in two f16 halves,
+//    d_x*S_j split into two f16 halves) go through v_mfma_f32_16x16x32_f16
+//    straight into the f32 output accumulator, four super-blocks per MFMA, so
+//    it needs no per-super-block epilogue.  Per token, d_x is pre-scaled by a
+//    power of two so the f16 halves cannot overflow; the output is scaled back
+//    exactly at the end.
+//
+// Work-group: 256 threads = 4 waves, 64 weight rows (16 per wave) x up to 160
+// tokens (TB blocks of 16).  Activations of one super-block are staged in LDS
+// and shared by the 4 waves; each wave unpacks only its own 16 rows.  K may be
+// split across work-groups (grid.y); partial tiles then go to a workspace and a
+// second kernel sums them in split order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dllm {
+
+constexpr int NT = 64;           // weight rows per work-group
+constexpr int ACT_STRIDE = 272;  // LDS bytes per token row (256 + 16: spreads banks)
+
+template <int QT>
+struct QTr;
+template <>
+struct QTr<QT_Q4K> {
+  static constexpr int BYTES = Q4K_BYTES;
+  static constexpr int SHIFT = 3;
+  static constexpr int RAW = 12;  // dwords of raw block data per lane
+};
+template <>
+struct QTr<QT_Q6K> {
+  static constexpr int BYTES = Q6K_BYTES;
+  static constexpr int SHIFT = 7;
+  static constexpr int RAW = 17;
+};
+
+
+
+__device__ __forceinline__ uint32_t pkmul(uint32_t a, uint32_t b) {
+  return as_u32(as_u16x2(a) * as_u16x2(b));
+}
+
+// Raw (packed) bytes of the lane's part of one weight super-block at byte
+// offset `off` of the weight buffer.  Reads past the end of the buffer (rows
+// beyond N) return zeros, so padded rows contribute nothing.
+template <int QT>
+__device__ __forceinline__ void load_raw(rsrc_t wr, uint32_t off, int g4, uint32_t (&raw)[QTr<QT>::RAW]) {
+  if constexpr (QT == QT_Q4K) {
+    // header (d | dmin, 12 scale/min bytes) and, per chunk c, the 8 nibble
+    // bytes at 16 + 32c + 8 g4.
+    const v4u hdr = buf_ld128(wr, off);
+    raw[0] = hdr[0]; raw[1] = hdr[1]; raw[2] = hdr[2]; raw[3] = hdr[3];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const v2u v = buf_ld64(wr, off + 16 + 32 * c + 8 * g4);
+      raw[4 + 2 * c] = v[0];
+      raw[5 + 2 * c] = v[1];
+    }
+  } else {
+    // per chunk c = (half h, quarter pair k1): low-nibble bytes at
+    // 64h + 32k1 + 8 g4; per half: high-bit bytes at 128 + 32h + 8 g4;
+    // 16 scale bytes at 192; f16 d at 208.  Blocks are 210 bytes, so a block
+    // may start 2 bytes past a dword boundary.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) buf_ld64_a2(wr, off + 64 * (c >> 1) + 32 * (c & 1) + 8 * g4, raw[2 * c], raw[2 * c + 1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) buf_ld64_a2(wr, off + 128 + 32 * h + 8 * g4, raw[8 + 2 * h], raw[9 + 2 * h]);
+    buf_ld64_a2(wr, off + 192, raw[12], raw[13]);
+    buf_ld64_a2(wr, off + 200, raw[14], raw[15]);
+    raw[16] = buf_ld16(wr, off + 208);
+  }
+}
+
+// Q6_K: four quants (bytes, 0..63) with one signed scale s -> the two int8
+// planes of s*(q-32).  In 16-bit lanes 2s*q - 64s = 2 s (q-32) = 256 hi + 2 lo,
+// so the high byte is hi and the low byte is 2 lo.
+__device__ __forceinline__ void q6_planes(uint32_t q, uint32_t s2, uint32_t c64, uint32_t& lo, uint32_t& hi) {
+  const uint32_t e = __builtin_amdgcn_perm(0u, q, 0x0c020c00u);  // q0, q2 in u16 lanes
+  const uint32_t o = __builtin_amdgcn_perm(0u, q, 0x0c030c01u);  // q1, q3
+  const uint32_t we = as_u32(as_u16x2(e) * as_u16x2(s2) + as_u16x2(c64));
+  const uint32_t wo = as_u32(as_u16x2(o) * as_u16x2(s2) + as_u16x2(c64));
+  hi = __builtin_amdgcn_perm(wo, we, 0x07030501u);
+  lo = __builtin_amdgcn_perm(wo, we, 0x06020400u) >> 1;
+}
+
+// Unpack raw bytes into the two int8 planes of the four 16x64 A fragments and
+// return the super-block factor d.
+template <int QT>
+__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, v4i (&alo)[4], v4i (&ahi)[4]) {
+  if constexpr (QT == QT_Q4K) {
+    uint32_t sc03, sc47, mn03, mn47;
+    q4k_scales(raw[1], raw[2], raw[3], sc03, sc47, mn03, mn47);
+    const uint32_t sl03 = sc03 & 0x07070707u, sh03 = (sc03 >> 3) & 0x07070707u;
+    const uint32_t sl47 = sc47 & 0x07070707u, sh47 = (sc47 >> 3) & 0x07070707u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // sub-blocks 2c (low nibbles) and 2c+1 (high nibbles)
+      const uint32_t slv = (c < 2) ? sl03 : sl47, shv = (c < 2) ? sh03 : sh47;
+      const int je = (2 * c) & 3, jo = (2 * c + 1) & 3;
+      const uint32_t sle = splat_byte_u16x2(slv, je), slo = splat_byte_u16x2(slv, jo);
+      const uint32_t she = splat_byte_u16x2(shv, je), sho = splat_byte_u16x2(shv, jo);
+      const uint32_t v0 = raw[4 + 2 * c], v1 = raw[5 + 2 * c];
+      const uint32_t n0l = q4k_lo_nibbles(v0), n1l = q4k_lo_nibbles(v1);
+      const uint32_t n0h = q4k_hi_nibbles(v0), n1h = q4k_hi_nibbles(v1);
+      alo[c] = v4i{(int)pkmul(n0l, sle), (int)pkmul(n1l, sle), (int)pkmul(n0h, slo), (int)pkmul(n1h, slo)};
+      ahi[c] = v4i{(int)pkmul(n0l, she), (int)pkmul(n1l, she), (int)pkmul(n0h, sho), (int)pkmul(n1h, sho)};
+    }
+    return f16_bits_to_f32(raw[0]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int h = c >> 1, k1 = c & 1;
+      // scale index g = i/16 for quarters k1 and k1+2 at l = 8 g4 .. 8 g4 + 7
+      const int gl = 8 * h + 2 * k1 + (g4 >> 1), gh = gl + 4;
+      const int sl = (int)(int8_t)(raw[12 + (gl >> 2)] >> (8 * (gl & 3)));
+      const int sh = (int)(int8_t)(raw[12 + (gh >> 2)] >> (8 * (gh & 3)));
+      const uint32_t s2l = ((uint32_t)(2 * sl) & 0xFFFFu) * 0x10001u;
+      const uint32_t c64l = ((uint32_t)(-64 * sl) & 0xFFFFu) * 0x10001u;
+      const uint32_t s2h = ((uint32_t)(2 * sh) & 0xFFFFu) * 0x10001u;
+      const uint32_t c64h = ((uint32_t)(-64 * sh) & 0xFFFFu) * 0x10001u;
+      const uint32_t L0 = raw[2 * c], L1 = raw[2 * c + 1];
+      const uint32_t H0 = raw[8 + 2 * h], H1 = raw[9 + 2 * h];
+      uint32_t lo[4], hi[4];
+      q6_planes(q6k_quants(L0, H0, k1), s2l, c64l, lo[0], hi[0]);
+      q6_planes(q6k_quants(L1, H1, k1), s2l, c64l, lo[1], hi[1]);
+      q6_planes(q6k_quants(L0, H0, k1 + 2), s2h, c64h, lo[2], hi[2]);
+      q6_planes(q6k_quants(L1, H1, k1 + 2), s2h, c64h, lo[3], hi[3]);
+      alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+      ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    return f16_bits_to_f32(raw[16]);
+  }
+}
+
+// LDS byte offsets (within a token row) of the two 8-byte activation pieces
+// that pair with chunk c of lane group g4 (same K order as the A fragment).
+template <int QT>
+__device__ __forceinline__ int act_off0(int c, int g4) {
+  return (QT == QT_Q4K) ? 64 * c + 8 * g4 : 128 * (c >> 1) + 32 * (c & 1) + 8 * g4;
+}
+template <int QT>
+__device__ __forceinline__ int act_off1(int c, int g4) {
+  return act_off0<QT>(c, g4) + ((QT == QT_Q4K) ? 32 : 64);
+}
+
+__device__ __forceinline__ uint32_t f32_order_bits(float v) {
+  if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int QT, int TB, bool ARGMAX>
+__global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
+  constexpr int TOK = TB * 16;
+  constexpr int SHIFT = QTr<QT>::SHIFT;
+  constexpr int BYTES = QTr<QT>::BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t s_act[TOK * ACT_STRIDE];
+  __shared__ float s_dx[TOK];
+  __shared__ float s_esc[TOK];
+  // Q4_K min-term activation operands: [slot sb%4][token][hi8 | lo8] f16.
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[(QT == QT_Q4K) ? 4 * TOK * 16 : 8];
+  __shared__ uint64_t s_key[ARGMAX ? 4 * TOK : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int64_t N = p.N, SB = p.SB, M = p.M;
+  const int64_t m0 = (int64_t)blockIdx.z * TOK;
+  const int64_t sb_begin = (int64_t)blockIdx.y * p.sps;
+  const int64_t sb_end = (sb_begin + p.sps < SB) ? sb_begin + p.sps : SB;
+  const int64_t nrow = (int64_t)blockIdx.x * NT + wv * 16 + r;
+  const bool row_ok = nrow < N;
+  // Buffer resources: loads past num_records read as zero (rows >= N,
+  // tokens >= M).  The host guarantees both buffers are below 2 GiB.
+  const rsrc_t wr = make_rsrc(p.w, N * SB * BYTES);
+  const rsrc_t xr = make_rsrc(p.xq, M * SB * Q8K_BYTES);
+  const uint32_t wrow_off = (uint32_t)(nrow * SB * BYTES);
+
+  // Per-token power-of-two pre-scale (Q4_K: keeps the f16 halves of
+  // d_x * S_j in range); 1 for Q6_K.
+  if (tid < TOK) {
+    float esc = 1.0f;
+    if constexpr (QT == QT_Q4K) {
+      const int64_t m = m0 + tid;
+      float mx = 0.0f;
+      if (m < M)
+        for (int64_t sb = sb_begin; sb < sb_end; ++sb)
+          mx = fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, buf_ld32(xr, (uint32_t)((m * SB + sb) * Q8K_BYTES)))));
+      if (mx > 0.0f) {
+        int e = 0;
+        (void)frexpf(mx, &e);
+        e = e < -100 ? -100 : (e > 100 ? 100 : e);
+        esc = ldexpf(1.0f, -e);
+      }
+    }
+    s_esc[tid] = esc;
+  }
+  if constexpr (QT == QT_Q4K) {
+    for (int i = tid; i < 4 * TOK * 16; i += 256) s_amin[i] = (_Float16)0.0f;
+  }
+
+  v4f yacc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) yacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8h bmin_hi = {}, bmin_lo = {};
+
+  uint32_t raw[QTr<QT>::RAW];
+  load_raw<QT>(wr, wrow_off + (uint32_t)(sb_begin * BYTES), g4, raw);
+
+  for (int64_t sb = sb_begin; sb < sb_end; ++sb) {
+    uint32_t cur[QTr<QT>::RAW];
+#pragma unroll
+    for (int i = 0; i < QTr<QT>::RAW; ++i) cur[i] = raw[i];
+    if (sb + 1 < sb_end) load_raw<QT>(wr, wrow_off + (uint32_t)((sb + 1) * BYTES), g4, raw);
+    const int slot = (int)((sb - sb_begin) & 3);
+
+    __syncthreads();  // previous super-block's LDS reads are done
+    // ---- stage this super-block's activations (int8) and scales in LDS
+    {
+      // thread tid moves dword (tid & 63) of tokens (tid >> 6) + 4k
+      constexpr int PER = TOK / 4;
+      const uint32_t base = (uint32_t)(((m0 + (tid >> 6)) * SB + sb) * Q8K_BYTES) + 4 + 4 * (tid & 63);
+      const uint32_t step = (uint32_t)(4 * SB * Q8K_BYTES);
+      uint8_t* dst = s_act + (tid >> 6) * ACT_STRIDE + 4 * (tid & 63);
+      uint32_t v[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) v[k] = buf_ld32(xr, base + k * step);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) *(uint32_t*)(dst + 4 * k * ACT_STRIDE) = v[k];
+    }
+    if (tid < TOK) {
+      const uint32_t xoff = (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES);
+      const float dx = __builtin_bit_cast(float, buf_ld32(xr, xoff)) * s_esc[tid];
+      s_dx[tid] = dx;
+      if constexpr (QT == QT_Q4K) {
+        // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1}),
+        // split into f16 high and low halves.
+        _Float16* dst = s_amin + (slot * TOK + tid) * 16;
+        const v4u bs0 = buf_ld128(xr, xoff + 260), bs1 = buf_ld128(xr, xoff + 276);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pr = (j < 4) ? bs0[j] : bs1[j - 4];
+          const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
+          const float a = dx * (float)S;
+          const _Float16 hi = (_Float16)a;
+          dst[j] = hi;
+          dst[8 + j] = (_Float16)(a - (float)hi);
+        }
+      }
+    }
+    // ---- Q4_K: at the start of each group of four super-blocks, the weight
+    // side of the min term for super-block (group start + g4): -dmin * m_j.
+    if constexpr (QT == QT_Q4K) {
+      if (slot == 0) {
+        const int64_t sbm = sb + g4;
+        float bm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (row_ok && sbm < sb_end) {
+          const v4u hdr = buf_ld128(wr, wrow_off + (uint32_t)(sbm * BYTES));
+          uint32_t sc03, sc47, mn03, mn47;
+          q4k_scales(hdr[1], hdr[2], hdr[3], sc03, sc47, mn03, mn47);
+          const float ndmin = -f16_bits_to_f32(hdr[0] >> 16);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t mb = (j < 4) ? mn03 : mn47;
+            bm[j] = ndmin * (float)((mb >> (8 * (j & 3))) & 63u);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 hi = (_Float16)bm[j];
+          bmin_hi[j] = hi;
+          bmin_lo[j] = (_Float16)(bm[j] - (float)hi);
+        }
+      }
+    }
+    v4i alo[4], ahi[4];
+    const float drow = unpack<QT>(cur, g4, alo, ahi);
+    __syncthreads();  // activations staged
+
+    // ---- integer contraction on MFMA (two planes x four K chunks) and the
+    // super-block epilogue y += (d * d_x) * ((hi << shift) + lo), one token
+    // block at a time so only 8 accumulator registers are live.
+    float dsel[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dsel[i] = __shfl(drow, 4 * g4 + i);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const uint8_t* arow = s_act + (t * 16 + r) * ACT_STRIDE;
+      v4i accl = v4i{0, 0, 0, 0}, acch = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint2 b0 = *(const uint2*)(arow + act_off0<QT>(c, g4));
+        const uint2 b1 = *(const uint2*)(arow + act_off1<QT>(c, g4));
+        const v4i b = v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y};
+        accl = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[c], b, accl, 0, 0, 0);
+        acch = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[c], b, acch, 0, 0, 0);
+      }
+      const float dx = s_dx[t * 16 + r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = (acch[i] << SHIFT) + accl[i];
+        yacc[t][i] += (float)a * (dsel[i] * dx);
+      }
+    }
+    // ---- Q4_K min term, once per four super-blocks (or at the range end)
+    if constexpr (QT == QT_Q4K) {
+      if (slot == 3 || sb + 1 == sb_end) {
+        if (slot != 3 && g4 > slot) {
+          bmin_hi = v8h{};
+          bmin_lo = v8h{};
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const _Float16* src = s_amin + (g4 * TOK + t * 16 + r) * 16;
+          const v8h ahv = *(const v8h*)src;
+          const v8h alv = *(const v8h*)(src + 8);
+          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, ahv, yacc[t], 0, 0, 0);
+          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, alv, yacc[t], 0, 0, 0);
+          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_lo, ahv, yacc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- write out: lane holds rows n0 + 4 g4 + i (i < 4) of token t*16 + r
+  const int64_t nbase = (int64_t)blockIdx.x * NT + wv * 16 + 4 * g4;
+  float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const int64_t m = m0 + t * 16 + r;
+    const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
+    v4f yv = yacc[t] * inv;
+    yacc[t] = yv;
+    if (m < M) {
+      float* dst = outp + m * p.ldo + nbase;
+      if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
+        *(v4f*)dst = yv;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nbase + i < N) dst[i] = yv[i];
+      }
+    }
+  }
+
+  if constexpr (ARGMAX) {
+    // per token: best (value, lowest row index) over this work-group's rows
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = nbase + i;
+        if (n < N) {
+          const uint64_t key = ((uint64_t)f32_order_bits(yacc[t][i]) << 32) | (uint64_t)(~(uint32_t)n);
+          best = key > best ? key : best;
+        }
+      }
+      const uint64_t o1 = __shfl_xor(best, 16);
+      best = o1 > best ? o1 : best;
+      const uint64_t o2 = __shfl_xor(best, 32);
+      best = o2 > best ? o2 : best;
+      if (g4 == 0) s_key[wv * TOK + t * 16 + r] = best;
+    }
+    __syncthreads();
+    if (tid < TOK) {
+      const int64_t m = m0 + tid;
+      uint64_t best = s_key[tid];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
+      if (m < M) p.keys[(int64_t)blockIdx.x * M + m] = best;
+    }
+  }
+}
+
+// Sum of the K-split partial tiles in split order (deterministic).
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int S, int64_t M,
+                                                    int64_t N, float* __restrict__ y, int64_t ldy) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  const int64_t m = i / N, n = i - m * N;
+  float acc = ws[i];
+  for (int s = 1; s < S; ++s) acc += ws[(int64_t)s * M * N + i];
+  y[m * ldy + n] = acc;
+}
+
+// argmax[m] = lowest row index of the largest logit, from per-tile keys.
+__global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restrict__ keys, int64_t n_tiles,
+                                                       int64_t M, int32_t* __restrict__ argmax) {
+  __shared__ uint64_t red[256];
+  const int64_t m = blockIdx.x;
+  uint64_t best = 0;
+  for (int64_t t = threadIdx.x; t < n_tiles; t += 256) {
+    const uint64_t k = keys[t * M + m];
+    best = k > best ? k : best;
+  }
+  red[threadIdx.x] = best;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s && red[threadIdx.x + s] > red[threadIdx.x]) red[threadIdx.x] = red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) argmax[m] = (int32_t)(~(uint32_t)(red[0] & 0xFFFFFFFFu));
+}
+
+// Test export: per-16 integer partial dots of the unsigned shared-form quants
+// with the Q8_K quants, through the same bit unpacking as the GEMM.
+template <int QT>
+__global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w, int64_t N, int64_t SB,
+                                                const uint8_t* __restrict__ xq, int64_t M,
+                                                int32_t* __restrict__ P) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N * SB * 16) return;
+  const int g = (int)(i & 15);
+  const int64_t sb = (i >> 4) % SB;
+  const int64_t n = ((i >> 4) / SB) % N;
+  const int64_t m = (i >> 4) / (SB * N);
+  const uint8_t* xr = xq + (m * SB + sb) * Q8K_BYTES + 4 + 16 * g;
+  int acc = 0;
+  for (int d = 0; d < 4; ++d) {
+    uint32_t u;
+    if constexpr (QT == QT_Q4K) {
+      const uint8_t* b = w + (n * SB + sb) * Q4K_BYTES;
+      const int j = g >> 1;
+      const uint32_t v = *(const uint32_t*)(b + 16 + 32 * (j >> 1) + 16 * (g & 1) + 4 * d);
+      u = (j & 1) ? q4k_hi_nibbles(v) : q4k_lo_nibbles(v);
+    } else {
+      const uint8_t* b = w + (n * SB + sb) * Q6K_BYTES;
+      const int h = g >> 3, k = (g >> 1) & 3, l = 16 * (g & 1) + 4 * d;
+      u = q6k_quants(ld_u32_a2(b + 64 * h + 32 * (k & 1) + l), ld_u32_a2(b + 128 + 32 * h + l), k);
+    }
+    const uint32_t q = *(const uint32_t*)(xr + 4 * d);
+    acc = __builtin_amdgcn_sdot4((int)q, (int)u, acc, false);  // u <= 63 is also a valid int8
+  }
+  P[i] = acc;
+}
+
+// ---- host-side launch helpers -------------------------------------------
+template <int QT, int TB, bool ARGMAX>
+static hipError_t launch_tb(const GemmParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_qgemm<QT, TB, ARGMAX>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int QT, bool ARGMAX>
+static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s) {
+  switch (tb) {
+    case 1: return launch_tb<QT, 1, ARGMAX>(p, grid, s);
+    case 2: return launch_tb<QT, 2, ARGMAX>(p, grid, s);
+    case 3: return launch_tb<QT, 3, ARGMAX>(p, grid, s);
+    case 4: return launch_tb<QT, 4, ARGMAX>(p, grid, s);
+    case 5: return launch_tb<QT, 5, ARGMAX>(p, grid, s);
+    case 6: return launch_tb<QT, 6, ARGMAX>(p, grid, s);
+    case 7: return launch_tb<QT, 7, ARGMAX>(p, grid, s);
+    case 8: return launch_tb<QT, 8, ARGMAX>(p, grid, s);
+    case 9: return launch_tb<QT, 9, ARGMAX>(p, grid, s);
+    default: return launch_tb<QT, 10, ARGMAX>(p, grid, s);
+  }
+}
+
+hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, dim3 grid, bool argmax, hipStream_t s) {
+  if (qtype == QT_Q4K) return argmax ? launch_q<QT_Q4K, true>(p, tb, grid, s) : launch_q<QT_Q4K, false>(p, tb, grid, s);
+  return argmax ? launch_q<QT_Q6K, true>(p, tb, grid, s) : launch_q<QT_Q6K, false>(p, tb, grid, s);
+}
+
+hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
+  const int64_t total = M * N;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, ws, S, M, N, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3((unsigned)M), dim3(256), 0, s, keys, n_tiles, M, argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_partials(int qtype, const uint8_t* w, int64_t N, int64_t SB, const uint8_t* xq, int64_t M,
+                           int32_t* P, hipStream_t s) {
+  const int64_t total = M * N * SB * 16;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (qtype == QT_Q4K)
+    hipLaunchKernelGGL(k_partials<QT_Q4K>, grid, dim3(256), 0, s, w, N, SB, xq, M, P);
+  else
+    hipLaunchKernelGGL(k_partials<QT_Q6K>, grid, dim3(256), 0, s, w, N, SB, xq, M, P);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

@@ -1,0 +1,142 @@
+/*
+ * libdllm -- the per-denoising-step quantized GEMM stream of a diffusion LM,
+ * as hand-written HIP kernels for CDNA4 (gfx950).
+ *
+ * A diffusion-LM denoising step reruns the whole bidirectional transformer
+ * over the whole canvas (L ~ 100..160 tokens), so every linear layer is a GEMM
+ * of L per-token int8 activation rows against GGUF Q4_K / Q6_K weight rows
+ * (mojo-dllm Development plan, "Compute design"; README "How it works").
+ *
+ * Conventions for every call:
+ *  - All buffer pointers are caller-owned DEVICE pointers on the current HIP
+ *    device; the library allocates nothing, keeps no state beyond its code
+ *    object and never synchronizes.  `stream` is a hipStream_t (NULL = the
+ *    null stream); work is only enqueued.
+ *  - Sizes are int64_t.  K is always a multiple of 256 (one super-block).
+ *  - Weights are row-major in GGUF order: row n (one output feature) is K/256
+ *    consecutive super-blocks.  Activations are row-major per token.
+ *  - Return value: 0 on success, a negative DLLM_E_* code otherwise.  Argument
+ *    errors are detected on the host before anything is enqueued; the message
+ *    is available from dllm_last_error() (per thread, valid until the next call
+ *    on that thread).  Unsupported types fail with an explicit message and no
+ *    fallback (technical specification, "GGUF" and "Error handling" sections).
+ *    Device-side faults surface at the caller's next synchronization.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLLM_ABI_VERSION 1
+
+/* qtype tags: the GGUF tensor-type ids. */
+#define DLLM_Q4_K 12
+#define DLLM_Q6_K 14
+#define DLLM_Q8_K 15
+
+#define DLLM_QK_K 256          /* values per super-block */
+#define DLLM_Q4_K_BYTES 144    /* f16 d | f16 dmin | 12 B scales/mins | 128 B 4-bit quants */
+#define DLLM_Q6_K_BYTES 210    /* 128 B low 4 bits | 64 B high 2 bits | 16 int8 scales | f16 d */
+#define DLLM_Q8_K_BYTES 292    /* f32 d | 256 int8 quants | 16 int16 sums */
+#define DLLM_DECODED_BYTES 356 /* f32 D | f32 off[16] | int16 sc[16] | uint8 u[256] */
+
+#define DLLM_OK 0
+#define DLLM_E_ARG (-1)         /* null pointer, bad leading dimension */
+#define DLLM_E_SHAPE (-2)       /* K % 256 != 0, M <= 0, N <= 0, n_rows out of [1, M] */
+#define DLLM_E_UNSUPPORTED (-3) /* qtype without a matrix kernel */
+#define DLLM_E_ALIGN (-4)       /* pointer alignment not met */
+#define DLLM_E_HIP (-5)         /* HIP runtime error at launch */
+#define DLLM_E_WORKSPACE (-6)   /* workspace smaller than the call needs */
+
+int dllm_abi_version(void);
+const char *dllm_last_error(void);
+
+/*
+ * Q8_K activation quantization (Development plan, "Compute design", first
+ * bullet: per token, int8 quants with one f32 scale per 256 values plus int
+ * sums per 16 values).  Block rule (the GGUF Q8_K definition): the pivot is the
+ * first value of largest magnitude in the 256-block; iscale = -127/pivot (f32,
+ * correctly rounded); q = min(127, round-half-even(f32(iscale * x))); d =
+ * 1/iscale; bsums[g] = sum of q[16g .. 16g+15].  An all-zero block gives d = 0,
+ * q = 0, bsums = 0.  Inputs must be finite.
+ *   x      f32 [M][ldx], 4-byte aligned, ldx >= K
+ *   y_q8k  [M][K/256] records of 292 bytes, 4-byte aligned (written)
+ * The output is bit-identical to the format definition.
+ */
+int dllm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
+                      void *y_q8k, void *stream);
+
+/*
+ * Decode Q4_K / Q6_K super-blocks into the shared form both types reduce to
+ * (Development plan, "Compute design", second bullet: unsigned bytes, an int16
+ * scale per 16 and an f32 offset per 16; the super-block factor D is kept as a
+ * leading f32), so that w_i = D * sc[i/16] * u[i] + off[i/16] exactly:
+ *   Q4_K: u = 4-bit quant, sc[g] = scale[g/2], off[g] = -(f32(dmin) * min[g/2])
+ *   Q6_K: u = 6-bit quant (0..63), sc[g] = scale[g], off[g] = -(32 f32(d) sc[g])
+ *   w    n_superblocks consecutive blocks (144 or 210 bytes), 2-byte aligned
+ *   out  n_superblocks records of 356 bytes, 4-byte aligned (written)
+ * Every field is exact, so the output is bit-exact.
+ */
+int dllm_decode_qk(int qtype, const void *w, int64_t n_superblocks,
+                   void *out_decoded, void *stream);
+
+/*
+ * Quantized GEMM y[m][n] = sum_k W_hat[n][k] * X_hat[m][k] for the masked-free
+ * linear layers (technical specification section 10 "Quantized Compute",
+ * kernel API linear_q4k(x, weight, out); Development plan "Compute design").
+ *   qtype   DLLM_Q4_K or DLLM_Q6_K
+ *   w       [N][K/256] weight super-blocks, 4-byte aligned
+ *   x_q8k   [M][K/256] Q8_K records (from dllm_quantize_q8k), 4-byte aligned
+ *   y       f32 [M][ldy], ldy >= N, 4-byte aligned (written, not accumulated)
+ *   workspace / workspace_bytes   optional scratch for splitting K across
+ *           work-groups; NULL/0 runs without a split.  A split needs
+ *           dllm_qgemm_workspace_bytes(qtype, N, K, M) bytes; with less the
+ *           call runs without a split.  The result agrees with the exact
+ *           dequantized product to f32 rounding either way.
+ */
+int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M);
+int dllm_qgemm(int qtype, const void *w, int64_t N, int64_t K,
+               const void *x_q8k, int64_t M, float *y, int64_t ldy,
+               void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Masked-row LM head (Development plan, "Compute design", last bullet; README
+ * "How it works", "Logits only where the sampler looks"): gather hidden rows
+ * rows[0..n_rows) of h, quantize each to Q8_K, multiply by the output matrix
+ * w [N][K] and write f32 logits plus the per-row argmax (greedy pick; lowest
+ * index among exactly equal logits).
+ *   h       f32 [M][ldh], ldh >= K
+ *   rows    int32 [n_rows] device array, each in [0, M) (not checked on the
+ *           host: an out-of-range index is undefined behaviour)
+ *   logits  f32 [n_rows][ldl], ldl >= N (written)
+ *   argmax  int32 [n_rows] (written)
+ *   workspace  at least dllm_lmhead_workspace_bytes(qtype, N, K, n_rows) bytes,
+ *           256-byte aligned (required)
+ * n_rows may be 1..M; the kernels are tuned for n_rows <= 32 (LLaDA's block).
+ */
+int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_rows);
+int dllm_lmhead_masked(int qtype, const void *w, int64_t N, int64_t K,
+                       const float *h, int64_t M, int64_t ldh,
+                       const int32_t *rows, int64_t n_rows, float *logits,
+                       int64_t ldl, int32_t *argmax, void *workspace,
+                       int64_t workspace_bytes, void *stream);
+
+/*
+ * Test export: per-16 integer partial dots of the shared form,
+ * P[m][n][sb][g] = sum_{t<16} u[n][256 sb + 16 g + t] * q[m][256 sb + 16 g + t]
+ * (u: the unsigned shared-form quant, q: the Q8_K int8 quant), int32, written
+ * as [M][N][K/256][16].  Uses the same in-register unpacking as dllm_qgemm.
+ * Meant for small shapes.
+ */
+int dllm_qgemm_partials_i32(int qtype, const void *w, int64_t N, int64_t K,
+                            const void *x_q8k, int64_t M, int32_t *P,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before anything is
+enqueued (technical specification, error-handling section: explicit,
+actionable messages; unsupported types fail with no fallback)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dllm.h")
+
+
+@pytest.fixture(scope="module")
+def dl():
+    import diffusion_lm_gemm_amd as dl
+    return dl
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dllm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function(dl):
+    names = _header_functions()
+    assert len(names) == 9
+    lib = ctypes.CDLL(dl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(dl.HEADER_EXPORTS) == names
+
+
+def test_abi_version_matches_header(dl):
+    v = int(re.search(r"#define DLLM_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert dl.abi_version() == v
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+
+
+def test_unsupported_type_message(dl):
+    rc = dl.lib.dllm_qgemm(8, FAKE, 64, 256, FAKE, 4, FAKE, 64, None, 0, None)
+    assert rc == dl.E_UNSUPPORTED
+    msg = dl.last_error()
+    assert "Q8_0" in msg and "Q4_K and Q6_K" in msg
+
+
+@pytest.mark.parametrize("K", [0, 100, 257, -256])
+def test_k_must_be_multiple_of_256(dl, K):
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, K, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_quantize_q8k(FAKE, 4, K, max(K, 1), FAKE, None) == dl.E_SHAPE
+
+
+def test_null_pointers(dl):
+    assert dl.lib.dllm_qgemm(dl.Q4_K, None, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ARG
+    assert "null" in dl.last_error()
+    assert dl.lib.dllm_qgemm(dl.Q6_K, FAKE, 64, 256, FAKE, 4, None, 64, None, 0, None) == dl.E_ARG
+    assert dl.lib.dllm_quantize_q8k(None, 4, 256, 256, FAKE, None) == dl.E_ARG
+    assert dl.lib.dllm_decode_qk(dl.Q4_K, None, 1, FAKE, None) == dl.E_ARG
+
+
+def test_bad_shapes_and_leading_dims(dl):
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 0, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, 0, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, 4, FAKE, 63, None, 0, None) == dl.E_ARG
+    assert dl.lib.dllm_quantize_q8k(FAKE, 4, 512, 500, FAKE, None) == dl.E_ARG
+    assert dl.lib.dllm_decode_qk(dl.Q6_K, FAKE, 0, FAKE, None) == dl.E_SHAPE
+
+
+def test_alignment(dl):
+    odd = ctypes.c_void_p((1 << 20) + 8)  # 8-byte aligned, not 16
+    assert dl.lib.dllm_qgemm(dl.Q4_K, odd, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
+    two = ctypes.c_void_p((1 << 20) + 2)
+    assert dl.lib.dllm_qgemm(dl.Q6_K, two, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
+    assert dl.lib.dllm_quantize_q8k(two, 4, 256, 256, FAKE, None) == dl.E_ALIGN
+
+
+def test_oversized_operands_rejected(dl):
+    # 2 GiB of Q4_K weights: the kernels address operands with 32-bit offsets
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 1 << 20, 4096 * 4, FAKE, 4, FAKE, 1 << 20, None, 0, None) == dl.E_SHAPE
+    assert "2 GiB" in dl.last_error()
+
+
+def test_lmhead_argument_errors(dl):
+    L = dl.lib
+    ok_ws = dl.lmhead_workspace_bytes(dl.Q6_K, 1000, 512, 4)
+    assert ok_ws > 0
+    ws = ctypes.c_void_p(1 << 24)
+    # n_rows outside [1, M]
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 3, 512, FAKE, 4, FAKE, 1000, FAKE, ws, ok_ws, None) == dl.E_SHAPE
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 3, 512, FAKE, 0, FAKE, 1000, FAKE, ws, ok_ws, None) == dl.E_SHAPE
+    # workspace too small, or missing
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE, ws, ok_ws - 1, None) == dl.E_WORKSPACE
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE, None, ok_ws, None) == dl.E_ARG
+    # ldl < N, ldh < K, unaligned workspace
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 999, FAKE, ws, ok_ws, None) == dl.E_ARG
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 256, FAKE, 4, FAKE, 1000, FAKE, ws, ok_ws, None) == dl.E_ARG
+    assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                ctypes.c_void_p((1 << 24) + 16), ok_ws, None) == dl.E_ALIGN
+
+
+def test_workspace_queries(dl):
+    # 4096 x 4096 at 148 tokens is split along K; a 126464-row LM head is not.
+    assert dl.qgemm_workspace_bytes(dl.Q4_K, 4096, 4096, 148) > 0
+    assert dl.qgemm_workspace_bytes(dl.Q6_K, 126464, 4096, 32) == 0
+    assert dl.qgemm_workspace_bytes(99, 4096, 4096, 148) == -1
+    assert dl.lmhead_workspace_bytes(dl.Q6_K, 126464, 4096, 32) >= 32 * 16 * 292

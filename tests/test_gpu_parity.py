@@ -1,0 +1,287 @@
+"""GPU parity: libdllm's HIP kernels (through the C ABI) against the CPU oracle.
+
+Bars (quantized GEMM stream of one denoising step; mojo-dllm Development plan,
+"Compute design"):
+  * Q8_K bytes, shared decoded form and per-16 int32 partials: bit-exact.
+  * f32 GEMM / LM-head outputs: |gpu - oracle| <= 1e-4 * (|oracle| + rms(row)),
+    rms(row) = RMS of the oracle's outputs for that token.
+  * LM-head argmax: identical to the oracle's, except where the oracle's top
+    two logits are closer than the tolerance (then several answers are
+    correct and the GPU's pick must be one of them); and always identical to
+    the argmax of the GPU's own f32 logits (same precision, lowest index).
+Inputs are seeded synthetic (synth/), shaped like LLaDA-8B's layers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dl():
+    import diffusion_lm_gemm_amd as dl
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return dl
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def assert_close_rows(y_gpu: np.ndarray, y_ref: np.ndarray, what: str):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    assert y_gpu.shape == y_ref.shape, what
+    rms = np.sqrt(np.mean(y_ref ** 2, axis=1, keepdims=True))
+    bound = TOL * (np.abs(y_ref) + rms)
+    err = np.abs(y_gpu - y_ref)
+    ratio = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    _say(f"{what}: max err/bound = {ratio:.3g}")
+    assert np.all(np.isfinite(y_gpu)), what
+    assert np.all(err <= bound), f"{what}: max err/bound {ratio}"
+
+
+def _weights(qtype, N, K, seed, name):
+    return synth.qk_rows(qtype, N, K, seed, name)
+
+
+# ---------------------------------------------------------------- Q8_K ----
+@pytest.mark.parametrize("M,K,pad", [(1, 256, 0), (17, 512, 0), (148, 4096, 0), (148, 12288, 0), (33, 1024, 64)])
+def test_quantize_q8k_bitexact(dl, M, K, pad):
+    _say(f"quantize M={M} K={K} pad={pad}")
+    x = synth.normal_f32((M, K + pad), 11, f"q8k-{M}-{K}")
+    x = x * torch.logspace(-3, 3, M).unsqueeze(1)  # spread of magnitudes
+    ref = oracle.quantize_q8k(x[:, :K].numpy())
+    got = dl.quantize_q8k(x.to(DEV)[:, :K]).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_q8k_edge_blocks(dl):
+    K = 256 * 8
+    x = torch.zeros((6, K))
+    x[1, 5], x[1, 300] = -3.0, 3.0            # magnitude tie: first index wins
+    x[2, :] = 1e-30                            # tiny values
+    x[2, 777] = -2e-30
+    x[3, :] = torch.linspace(-1e30, 1e30, K)   # huge values
+    x[4, ::3] = 0.5                            # exact half-way products
+    x[4, 1::3] = -0.25
+    x[5, :] = synth.normal_f32((K,), 5, "edge")
+    x[5, 256:512] = 0.0                        # an all-zero block inside a row
+    ref = oracle.quantize_q8k(x.numpy())
+    got = dl.quantize_q8k(x.to(DEV)).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_gather_quantize_through_lmhead_equals_plain_quantize(dl):
+    # the LM head's gather+quantize must feed the GEMM the same Q8_K bytes as
+    # quantizing the gathered rows directly: compare logits with qgemm on them.
+    N, K, M = 192, 512, 40
+    w = _weights(dl.Q6_K, N, K, 21, "w").to(DEV)
+    h = synth.normal_f32((M, K), 21, "h").to(DEV)
+    rows = torch.tensor([39, 0, 17, 17, 5], dtype=torch.int32, device=DEV)
+    logits, _ = dl.lmhead_masked(dl.Q6_K, w, N, K, h, rows)
+    xq = dl.quantize_q8k(h[rows.long()].contiguous())
+    y = dl.qgemm(dl.Q6_K, w, N, K, xq, rows.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(logits, y)
+
+
+# -------------------------------------------------------------- decode ----
+@pytest.mark.parametrize("qtype", [12, 14])
+@pytest.mark.parametrize("nsb", [1, 33, 1024])
+def test_decode_bitexact(dl, qtype, nsb):
+    _say(f"decode qtype={qtype} nsb={nsb}")
+    w = _weights(qtype, nsb, 256, 3, f"dec-{nsb}")
+    if qtype == 14:
+        w.view(nsb, 210)[0, 192:208] = torch.tensor([-128] * 8 + [127] * 8, dtype=torch.int8).view(torch.uint8)
+    ref = oracle.decode_shared(qtype, w.numpy(), nsb)
+    got = dl.decode_qk(qtype, w.to(DEV), nsb).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------ partials ----
+@pytest.mark.parametrize("qtype", [12, 14])
+def test_partials_bitexact(dl, qtype):
+    N, K, M = 37, 768, 5
+    w = _weights(qtype, N, K, 4, "p")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 4, "px").numpy())
+    ref = oracle.partials(qtype, w.numpy(), N, K, xq, M)
+    got = dl.qgemm_partials_i32(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- GEMM ----
+SHAPES = [(1, 1, 256), (17, 70, 512), (148, 200, 1024), (33, 64, 2048), (161, 65, 768), (160, 128, 4096),
+          (5, 300, 3072)]
+
+
+@pytest.mark.parametrize("qtype", [12, 14])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("split", [False, True])
+def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
+    _say(f"qgemm qtype={qtype} M={M} N={N} K={K} split={split}")
+    w = _weights(qtype, N, K, 7, f"g-{N}-{K}")
+    x = synth.normal_f32((M, K), 7, f"gx-{M}-{K}")
+    xq = oracle.quantize_q8k(x.numpy())
+    ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
+    ws = None
+    if split:
+        nb = max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    assert_close_rows(y, ref, f"qgemm {qtype} {M}x{N}x{K} split={split}")
+
+
+@pytest.mark.parametrize("qtype,N,K", [(12, 4096, 4096), (14, 4096, 12288)])
+def test_qgemm_full_size_layers(dl, qtype, N, K):
+    """Single LLaDA-8B linear layers at L = 148: attn_q (Q4_K 4096x4096) and
+    attn_v/ffn_down-shaped Q6_K (4096x12288), in the bench's launch
+    configuration (with the K-split workspace), against the full oracle."""
+    M = 148
+    _say(f"full-size qgemm qtype={qtype} N={N} K={K}")
+    w = _weights(qtype, N, K, 42, f"layer-{qtype}-{N}-{K}")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 42, f"act-{K}").numpy())
+    ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
+    ws = torch.empty(max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    assert_close_rows(y, ref, f"full qgemm {qtype} {N}x{K}")
+
+
+def test_qgemm_gate_up_shape_sampled(dl):
+    """gate/up grouped (Q4_K, N = 2 x 12288, K = 4096) at L = 148: sampled
+    outputs one by one, plus whole oracle rows for four tokens."""
+    qtype, N, K, M = 12, 24576, 4096, 148
+    w = _weights(qtype, N, K, 42, "gateup")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 42, "gateup-x").numpy())
+    ws = torch.empty(max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    toks = [0, 57, 146, 147]
+    ref_rows = oracle.gemm(qtype, w.numpy(), N, K, xq[toks], len(toks))
+    assert_close_rows(y[toks], ref_rows, "gate/up full rows")
+    rng = np.random.default_rng(0)
+    mi = rng.integers(0, M, 3000)
+    ni = rng.integers(0, N, 3000)
+    ref = oracle.gemm_sample(qtype, w.numpy(), N, K, xq, M, mi, ni)
+    rms = float(np.sqrt(np.mean(ref_rows ** 2)))
+    err = np.abs(y[mi, ni] - ref)
+    assert np.all(err <= TOL * (np.abs(ref) + rms)), float(err.max())
+
+
+def test_qgemm_integer_special_case_exact(dl):
+    """d = 1, dmin = 0, unit scales, d_x = 1: every partial sum is an integer
+    below 2^24, so the f32 result must equal the integer dot product."""
+    from ggufpack import pack_q4k, pack_q8k
+    rng = np.random.default_rng(3)
+    N, M, K = 64, 20, 1024
+    u = rng.integers(0, 16, (N, K))
+    q = rng.integers(-127, 128, (M, K))
+    w = np.stack([np.concatenate([pack_q4k(0x3C00, 0, [1] * 8, [0] * 8, u[n, 256 * s:256 * s + 256])
+                                  for s in range(K // 256)]) for n in range(N)])
+    xq = np.stack([np.concatenate([pack_q8k(1.0, q[m, 256 * s:256 * s + 256]) for s in range(K // 256)])
+                   for m in range(M)])
+    y = dl.qgemm(12, torch.from_numpy(w).to(DEV), N, K, torch.from_numpy(xq).to(DEV), M).cpu().numpy()
+    assert np.array_equal(y.astype(np.int64), q @ u.T)
+
+
+def test_qgemm_zero_weights_and_strided_output(dl):
+    N, K, M = 100, 512, 30
+    w = torch.zeros((N, K // 256 * 210), dtype=torch.uint8, device=DEV)
+    xq = dl.quantize_q8k(synth.normal_f32((M, K), 2, "z").to(DEV))
+    big = torch.full((M, N + 28), 7.0, device=DEV)
+    dl.qgemm(14, w, N, K, xq, M, y=big[:, :N])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(big[:, :N]) == 0
+    assert torch.all(big[:, N:] == 7.0)
+
+
+def test_qgemm_deterministic(dl):
+    N, K, M = 4096, 4096, 148
+    w = _weights(12, N, K, 9, "det").to(DEV)
+    xq = dl.quantize_q8k(synth.normal_f32((M, K), 9, "detx").to(DEV))
+    ws = torch.empty(max(dl.qgemm_workspace_bytes(12, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    a = dl.qgemm(12, w, N, K, xq, M, workspace=ws).clone()
+    b = dl.qgemm(12, w, N, K, xq, M, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- LM head ----
+def _check_argmax(logits_gpu, am_gpu, ref_logits, ref_am, what):
+    lg = np.asarray(logits_gpu, np.float64)
+    # same precision: the kernel's pick is the argmax (lowest index) of its own f32 logits
+    assert np.array_equal(am_gpu, np.argmax(np.asarray(logits_gpu), axis=1)), what
+    rms = np.sqrt(np.mean(ref_logits ** 2, axis=1))
+    exceptions = 0
+    for r in range(ref_logits.shape[0]):
+        if am_gpu[r] == ref_am[r]:
+            continue
+        top = np.sort(ref_logits[r])[-2:]
+        tol = 2 * TOL * (abs(top[1]) + rms[r])
+        assert top[1] - top[0] <= tol, f"{what}: row {r} argmax {am_gpu[r]} != {ref_am[r]}"
+        assert ref_logits[r, am_gpu[r]] >= top[1] - tol
+        exceptions += 1
+    _say(f"{what}: argmax identical in {ref_logits.shape[0] - exceptions}/{ref_logits.shape[0]} rows")
+
+
+@pytest.mark.parametrize("n_rows", [1, 7, 32, 40])
+def test_lmhead_small(dl, n_rows):
+    N, K, M = 1000, 512, 148
+    w = _weights(14, N, K, 13, "lm-small")
+    h = synth.normal_f32((M, K), 13, "lm-h")
+    rows = synth.distinct_rows(n_rows, M, 13, f"rows-{n_rows}")
+    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
+    logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    logits = logits.cpu().numpy(); am = am.cpu().numpy()
+    assert_close_rows(logits, ref, f"lmhead n_rows={n_rows}")
+    _check_argmax(logits, am, ref, ref_am, f"lmhead n_rows={n_rows}")
+
+
+def test_lmhead_q4k_and_ragged_vocab(dl):
+    N, K, M = 777, 768, 50
+    w = _weights(12, N, K, 14, "lm-q4")
+    h = synth.normal_f32((M, K), 14, "lm-q4h")
+    rows = synth.distinct_rows(9, M, 14, "rows")
+    ref, ref_am = oracle.lmhead(12, w.numpy(), N, K, h.numpy(), rows.numpy())
+    logits, am = dl.lmhead_masked(12, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    assert_close_rows(logits.cpu().numpy(), ref, "lmhead q4k")
+    _check_argmax(logits.cpu().numpy(), am.cpu().numpy(), ref, ref_am, "lmhead q4k")
+
+
+def test_lmhead_exact_tie_picks_lowest_index(dl):
+    N, K, M = 300, 256, 8
+    w = _weights(14, N, K, 15, "tie")
+    w[200] = w[77]
+    w[250] = w[77]
+    # make row 77's copies dominate for hidden row 3 by aligning h with them
+    wh = oracle.decode_rows(14, w.numpy(), N, K)
+    h = synth.normal_f32((M, K), 15, "tie-h")
+    h[3] = torch.from_numpy(np.sign(wh[77]).astype(np.float32))
+    rows = torch.tensor([3, 1], dtype=torch.int32)
+    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
+    assert ref_am[0] == 77
+    logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    am = am.cpu().numpy()
+    lg = logits.cpu().numpy()
+    assert lg[0, 77] == lg[0, 200] == lg[0, 250]
+    assert am[0] == 77
+
+
+def test_lmhead_full_size(dl):
+    """Masked-row LM head: 32 masked canvas rows (20..51 of 148) x LLaDA's
+    untied 126464 x 4096 output matrix in Q6_K, against the full oracle."""
+    N, K, M = 126464, 4096, 148
+    _say("full-size lmhead")
+    w = _weights(14, N, K, 42, "output")
+    h = synth.normal_f32((M, K), 42, "hidden")
+    rows = torch.arange(20, 52, dtype=torch.int32)
+    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
+    logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    logits = logits.cpu().numpy(); am = am.cpu().numpy()
+    assert_close_rows(logits, ref, "lmhead full")
+    _check_argmax(logits, am, ref, ref_am, "lmhead full")
