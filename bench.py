@@ -1,0 +1,305 @@
+"""Benchmark: one denoising step's quantized GEMM stream on one MI355X.
+
+Workload (the whole-step stream of LLaDA-8B Q4_K_M at canvas L = 148; mojo-dllm
+Development plan, "Model facts used" and "Compute design"): 32 layers, each
+  quantize(x_norm) -> Q,K,V (4096x4096 each) -> quantize(attn) -> O (4096x4096)
+  -> quantize(h_norm) -> gate, up (12288x4096 each) -> quantize(act) -> down (4096x12288)
+with Q4_K weights except attn_v and ffn_down in Q6_K in the even layers (a
+reading of "half the layers"), then the masked-row LM head (32 masked rows
+20..51 of the canvas, 126464x4096 Q6_K, f32 logits + argmax).  Q,K,V share an
+input and run as one GEMM over their stacked rows when they share a type
+(K and V stacked likewise for gate/up); the arithmetic is unchanged.
+Weights and activations are seeded synthetic (synth/), resident in HBM before
+timing; every layer has its own weights (4.6 GB) and its own f32 inputs.
+
+A step is one replay of a HIP graph holding the whole stream.  Prints ONE
+JSON line (rank 0).  `value` is ms per step (lower is better).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per denoising-step GEMM stream (L=148) + int8 TOPS and % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+D, FFN, LAYERS, VOCAB = 4096, 12288, 32, 126464
+MASKED = 32
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--L", type=int, default=148, help="canvas tokens")
+    ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py runs on one GPU only: this build has no multi-GPU path "
+                  f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import diffusion_lm_gemm_amd as dl
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, seed = args.L, args.seed
+    Q4, Q6 = dl.Q4_K, dl.Q6_K
+
+    def bb(q):
+        return dl.block_bytes(q)
+
+    # ---------------- weights and inputs (resident before timing) ----------
+    t_setup = time.time()
+    layers = []
+    for l in range(LAYERS):
+        even = (l % 2 == 0)
+        lw = {"even": even}
+        if even:  # V is Q6_K: Q and K stacked, V alone
+            lw["qk"] = synth.q4k_rows(2 * D, D, seed, f"L{l:02d}.attn_qk", dev)
+            lw["v"] = synth.q6k_rows(D, D, seed, f"L{l:02d}.attn_v", dev)
+            lw["down"] = synth.q6k_rows(D, FFN, seed, f"L{l:02d}.ffn_down", dev)
+        else:
+            lw["qkv"] = synth.q4k_rows(3 * D, D, seed, f"L{l:02d}.attn_qkv", dev)
+            lw["down"] = synth.q4k_rows(D, FFN, seed, f"L{l:02d}.ffn_down", dev)
+        lw["o"] = synth.q4k_rows(D, D, seed, f"L{l:02d}.attn_output", dev)
+        lw["gu"] = synth.q4k_rows(2 * FFN, D, seed, f"L{l:02d}.ffn_gate_up", dev)
+        lw["x_norm"] = synth.normal_f32((L, D), seed, f"L{l:02d}.x_norm", dev)
+        lw["attn"] = synth.normal_f32((L, D), seed, f"L{l:02d}.attn", dev)
+        lw["h_norm"] = synth.normal_f32((L, D), seed, f"L{l:02d}.h_norm", dev)
+        lw["act"] = synth.normal_f32((L, FFN), seed, f"L{l:02d}.act", dev)
+        layers.append(lw)
+    w_out = synth.q6k_rows(VOCAB, D, seed, "output", dev)
+    hidden = synth.normal_f32((L, D), seed, "hidden", dev)
+    rows = torch.arange(20, 20 + MASKED, dtype=torch.int32, device=dev)
+
+    xq_d = torch.empty((L, D // 256 * 292), dtype=torch.uint8, device=dev)
+    xq_f = torch.empty((L, FFN // 256 * 292), dtype=torch.uint8, device=dev)
+    y_qkv = torch.empty((L, 3 * D), dtype=torch.float32, device=dev)
+    y_o = torch.empty((L, D), dtype=torch.float32, device=dev)
+    y_gu = torch.empty((L, 2 * FFN), dtype=torch.float32, device=dev)
+    y_down = torch.empty((L, D), dtype=torch.float32, device=dev)
+    logits = torch.empty((MASKED, VOCAB), dtype=torch.float32, device=dev)
+    amax = torch.empty(MASKED, dtype=torch.int32, device=dev)
+    ws_bytes = max(dl.qgemm_workspace_bytes(q, n, k, L) for q, n, k in
+                   [(Q4, 3 * D, D), (Q4, 2 * D, D), (Q6, D, D), (Q4, D, D), (Q4, 2 * FFN, D),
+                    (Q4, D, FFN), (Q6, D, FFN)])
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(dl.lmhead_workspace_bytes(Q6, VOCAB, D, MASKED), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    # ---------------- the step as a list of calls --------------------------
+    calls = []  # (kind, fn, algorithmic bytes, int8 ops)
+
+    def add_quant(x, out):
+        M, K = x.shape
+        calls.append(("quantize_q8k", lambda: dl.quantize_q8k(x, out), M * K * 4 + M * K // 256 * 292, 0))
+
+    def add_gemm(q, w, N, K, xq, y):
+        byts = N * K // 256 * bb(q) + L * K // 256 * 292 + L * N * 4
+        kind = "qgemm_q4k" if q == Q4 else "qgemm_q6k"
+        calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws), byts, 2 * L * N * K))
+
+    for lw in layers:
+        add_quant(lw["x_norm"], xq_d)
+        if lw["even"]:
+            add_gemm(Q4, lw["qk"], 2 * D, D, xq_d, y_qkv[:, :2 * D])
+            add_gemm(Q6, lw["v"], D, D, xq_d, y_qkv[:, 2 * D:])
+        else:
+            add_gemm(Q4, lw["qkv"], 3 * D, D, xq_d, y_qkv)
+        add_quant(lw["attn"], xq_d)
+        add_gemm(Q4, lw["o"], D, D, xq_d, y_o)
+        add_quant(lw["h_norm"], xq_d)
+        add_gemm(Q4, lw["gu"], 2 * FFN, D, xq_d, y_gu)
+        add_quant(lw["act"], xq_f)
+        add_gemm(Q6 if lw["even"] else Q4, lw["down"], D, FFN, xq_f, y_down)
+    lm_bytes = (MASKED * D * 4 + MASKED * D // 256 * 292 + VOCAB * D // 256 * bb(Q6)
+                + MASKED * VOCAB * 4 + MASKED * 4)
+    calls.append(("lmhead_q6k", lambda: dl.lmhead_masked(Q6, w_out, VOCAB, D, hidden, rows, logits, amax, ws_lm),
+                  lm_bytes, 2 * MASKED * VOCAB * D))
+    step_bytes = sum(c[2] for c in calls)
+    step_ops = sum(c[3] for c in calls)
+
+    def run_step():
+        for c in calls:
+            c[1]()
+
+    # ---------------- graph capture and timed replays ----------------------
+    run_step()  # eager warm-up (also loads every code object)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            run_step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] setup {t_setup:.1f}s; {len(calls)} calls/step; graph: {ms_step:.4f} ms/step "
+          f"(wall {1e3 * wall / args.steps:.4f} ms/step)", file=sys.stderr, flush=True)
+
+    # ---------------- per-call durations (eager, HIP events on the launch stream)
+    reps = 3
+    per = {}
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    for _ in range(reps):
+        for (a, b), c in zip(evs, calls):
+            a.record()
+            c[1]()
+            b.record()
+        torch.cuda.synchronize()
+        for (a, b), c in zip(evs, calls):
+            k = per.setdefault(c[0], [0.0, 0, 0, 0])
+            k[0] += a.elapsed_time(b)
+            k[1] += 1
+            k[2] += c[2]
+            k[3] += c[3]
+    kinds = {}
+    for k, (ms, n, byts, ops) in per.items():
+        kinds[k] = {"launches_per_step": n // reps, "avg_ms": ms / n,
+                    "GBps": byts / (ms * 1e-3) / 1e9, "TOPS": ops / (ms * 1e-3) / 1e12 if ops else 0.0,
+                    "share_of_eager_time": 0.0}
+    tot = sum(v[0] for v in per.values())
+    for k in kinds:
+        kinds[k]["share_of_eager_time"] = per[k][0] / tot
+    dom = max(per, key=lambda k: per[k][0])
+    dms, dn, dbytes, dops = per[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
+
+    # ---------------- HBM traffic from committed counter summaries ---------
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_step_L{L}.txt")
+    if os.path.exists(tpath):
+        kv = dict(l.split("=", 1) for l in open(tpath).read().split() if "=" in l)
+        src_hash = _kernel_hash()
+        if kv.get("kernel_sha") == src_hash and "bytes_per_call" in kv:
+            traffic = float(kv["bytes_per_call"])
+
+    # ---------------- CPU oracle baseline (bounded sample) -----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, step_ops // 2)
+
+    step_s = ms_step * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"whole denoising-step GEMM stream, LLaDA-8B Q4_K_M shapes, L={L}: "
+                               f"32 layers (Q,K,V,O 4096x4096; gate,up 12288x4096; down 4096x12288; "
+                               f"attn_v/ffn_down Q6_K in even layers) + masked LM head 32x126464x4096 Q6_K",
+                   "L": L, "layers": LAYERS, "masked_rows": MASKED, "calls_per_step": len(calls),
+                   "launch": "one HIP graph replay per step"},
+        "step_int8_TOPS": round(step_ops / step_s / 1e12, 2),
+        "step_GBps": round(step_bytes / step_s / 1e9, 1),
+        "step_frac_hbm": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_frac_mfma": round(step_ops / step_s / 1e12 / INT8_PEAK_TOPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "step_int8_ops": step_ops,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_call_ms": round(dms / dn, 5), "calls_per_step": dn // reps,
+                     "algorithmic_bytes_per_call": dbytes // dn,
+                     "int8_TOPS": round(dops / (dms * 1e-3) / 1e12, 2),
+                     "frac_mfma": round(dops / (dms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)},
+        "per_call_kind": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                          for k, v in kinds.items()},
+        "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("common.hpp", "qgemm.hip", "quantize.hip"):
+        h.update(open(os.path.join(ROOT, "diffusion_lm_gemm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(args, step_macs: int):
+    """The oracle (plain f64 C, threads over output rows) on a bounded sample of
+    the step: Q4_K layers of 4096 x 4096 and Q6_K 4096 x 12288 rows at L
+    tokens, grown until about --cpu-seconds of CPU work, then scaled to ms per
+    step by the step's MAC count."""
+    import numpy as np
+    import oracle
+    import synth
+    L = args.L
+    nt = oracle.default_threads()
+    x4 = oracle.quantize_q8k(synth.normal_f32((L, D), 1, "cpu-x4").numpy())
+    x12 = oracle.quantize_q8k(synth.normal_f32((L, FFN), 1, "cpu-x12").numpy())
+    # one Q4_K 4096 x 4096 layer and one Q6_K 4096 x 12288 layer at L tokens,
+    # repeated until about --cpu-seconds have passed
+    w4 = synth.q4k_rows(D, D, 1, "cpu-w4").numpy()
+    w6 = synth.q6k_rows(D, FFN, 1, "cpu-w6").numpy()
+    macs, secs, reps = 0, 0.0, 0
+    t0 = time.perf_counter()
+    while secs < args.cpu_seconds:
+        oracle.gemm(12, w4, D, D, x4, L, nt)
+        oracle.gemm(14, w6, D, FFN, x12, L, nt)
+        reps += 1
+        macs += D * L * (D + FFN)
+        secs = time.perf_counter() - t0
+    rate = macs / secs
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(step_macs / rate * 1e3, 1), "unit": "ms", "cores": nt, "kind": "oracle",
+            "sample": f"{reps} x (oracle f64 GEMM of a Q4_K 4096x4096 layer + a Q6_K 4096x12288 layer at {L} tokens): "
+                      f"{macs / 1e9:.1f} G MAC in {secs:.2f} s = {rate / 1e9:.2f} GMAC/s, scaled to the step's "
+                      f"{step_macs / 1e12:.3f} T MAC",
+            "cpu": cpu_model or platform.processor()}
+
+
+if __name__ == "__main__":
+    main()
