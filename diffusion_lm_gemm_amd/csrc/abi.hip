@@ -94,32 +94,50 @@ int tb_for(int64_t M) {
   return (int)(tb > 10 ? 10 : tb);
 }
 
+constexpr int64_t kCUs = 256;  // MI355X compute units
+
 struct Plan {
   int tb;
+  int nw;   // waves per work-group: tile = 16 * nw weight rows
   int64_t n_tiles, m_tiles;
   int S;    // K splits
   int sps;  // super-blocks per split
 };
 
-// K is split only when the (row tile x token tile) grid is too small to give
-// every CU two work-groups; each split keeps at least four super-blocks.
-Plan plan_gemm(int64_t N, int64_t K, int64_t M) {
-  Plan p;
-  p.tb = tb_for(M);
-  p.n_tiles = cdiv(N, 64);
-  p.m_tiles = cdiv(M, 16 * p.tb);
+// Pick the tile height (64 or 128 rows) and the K split that minimise an
+// estimate of the makespan: work-group rounds over the CUs (one work-group
+// per CU at a time) times super-blocks per work-group, plus a charge for
+// writing and re-reading split partials.  With no workspace, S = 1.
+Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
+  Plan best{};
+  double best_cost = 1e300;
   const int64_t SB = K / 256;
-  const int64_t tiles = p.n_tiles * p.m_tiles;
-  const int64_t target = 512;
-  int64_t S = (tiles >= target) ? 1 : cdiv(target, tiles);
-  const int64_t smax = SB / 4 > 0 ? SB / 4 : 1;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  int64_t sps = cdiv(SB, S);
-  S = cdiv(SB, sps);
-  p.S = (int)S;
-  p.sps = (int)sps;
-  return p;
+  for (int nw : {8, 4}) {
+    // Q6_K at more than 128 tokens does not fit 8 waves' registers without spills
+    if (nw == 8 && qtype == DLLM_Q6_K && tb_for(M) >= 9) continue;
+    const int64_t rows = 16 * nw;
+    const int64_t n_tiles = cdiv(N, rows);
+    const int tb = tb_for(M);
+    const int64_t m_tiles = cdiv(M, 16 * tb);
+    const int64_t smax = allow_split ? (SB < 16 ? SB : 16) : 1;
+    for (int64_t S = 1; S <= smax; ++S) {
+      const int64_t sps = cdiv(SB, S);
+      const int64_t s_eff = cdiv(SB, sps);
+      if (s_eff != S) continue;
+      const int64_t wgs = n_tiles * m_tiles * S;
+      const int64_t rounds = cdiv(wgs, kCUs);
+      // unit: one super-block of a 64-row tile (~0.65 us); 128 rows cost 2.
+      // +1.5 for filling the pipeline; a split adds the reduction launch
+      // (~3 us) and moving S partial tiles of M x N f32 at ~4 TB/s.
+      double cost = (double)rounds * (double)sps * (rows / 64.0) + 1.5;
+      if (S > 1) cost += (3e-6 + (double)S * (double)M * (double)N * 4.0 / 4e12) / 0.65e-6;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = Plan{tb, nw, n_tiles, m_tiles, (int)S, (int)sps};
+      }
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -154,7 +172,7 @@ int dllm_decode_qk(int qtype, const void* w, int64_t n_superblocks, void* out, v
 
 int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M) {
   if (check_qtype(qtype) || N <= 0 || M <= 0 || K <= 0 || K % 256) return -1;
-  const Plan p = plan_gemm(N, K, M);
+  const Plan p = plan_gemm(qtype, N, K, M, true);
   return p.S > 1 ? (int64_t)p.S * M * N * 4 : 0;
 }
 
@@ -179,12 +197,10 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
   if (!y) return fail(DLLM_E_ARG, "dllm_qgemm: null output pointer");
   if (ldy < N) return fail(DLLM_E_ARG, "dllm_qgemm: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
   if (!aligned(y, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm: y must be 4-byte aligned");
-  Plan pl = plan_gemm(N, K, M);
+  Plan pl = plan_gemm(qtype, N, K, M, true);
   const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
-  if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) {
-    pl.S = 1;  // no usable workspace: run the whole K range per work-group
-    pl.sps = (int)(K / 256);
-  }
+  if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    pl = plan_gemm(qtype, N, K, M, false);  // no usable workspace: whole K range per work-group
   GemmParams p;
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
@@ -199,13 +215,13 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
     p.out = y;
     p.ldo = ldy;
     p.split_stride = 0;
-    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, grid, false, s), "dllm_qgemm launch"))) return rc;
+    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.nw, grid, false, s), "dllm_qgemm launch"))) return rc;
     return ok();
   }
   p.out = (float*)workspace;
   p.ldo = N;
   p.split_stride = M * N;
-  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, grid, false, s), "dllm_qgemm launch"))) return rc;
+  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.nw, grid, false, s), "dllm_qgemm launch"))) return rc;
   return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, s), "dllm_qgemm reduce launch");
 }
 
@@ -260,9 +276,9 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   p.split_stride = 0;
   p.sps = (int)SB;
   const int tb = tb_for(n_rows);
-  const int64_t n_tiles = cdiv(N, 64);
+  const int64_t n_tiles = cdiv(N, 64);  // 4 waves, 64 rows per work-group
   const dim3 grid((unsigned)n_tiles, 1, (unsigned)cdiv(n_rows, 16 * tb));
-  if ((rc = hip_status(launch_qgemm(qtype, p, tb, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
+  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 4, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
   return hip_status(launch_argmax_finalize(keys, n_tiles, n_rows, argmax, s), "dllm_lmhead_masked argmax launch");
 }
 

@@ -34,7 +34,6 @@
 
 namespace dllm {
 
-constexpr int NT = 64;           // weight rows per work-group
 constexpr int ACT_STRIDE = 272;  // LDS bytes per token row (256 + 16: spreads banks)
 
 template <int QT>
@@ -167,42 +166,46 @@ __device__ __forceinline__ uint32_t f32_order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int QT, int TB, bool ARGMAX>
-__global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
-  constexpr int TOK = TB * 16;
+template <int QT, int TB, int NW, bool ARGMAX>
+__global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
+  constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
+  constexpr int NTH = 64 * NW;          // threads
+  constexpr int ROWS = 16 * NW;         // weight rows per work-group
+  constexpr int STG = TOK / NW;         // activation dwords per thread per stage
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t s_act[TOK * ACT_STRIDE];
-  __shared__ float s_dx[TOK];
+  constexpr bool MINS = (QT == QT_Q4K);
+  // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
+  // ring (two groups of four super-blocks) of min-term activation operands
+  // [slot][token][hi8 | lo8] f16: one group is read while the next is written.
+  __shared__ __attribute__((aligned(16))) uint8_t s_act[2][TOK * ACT_STRIDE];
+  __shared__ float s_dx[2][TOK];
   __shared__ float s_esc[TOK];
-  // Q4_K min-term activation operands: [slot sb%4][token][hi8 | lo8] f16.
-  __shared__ __attribute__((aligned(16))) _Float16 s_amin[(QT == QT_Q4K) ? 4 * TOK * 16 : 8];
-  __shared__ uint64_t s_key[ARGMAX ? 4 * TOK : 1];
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 8 * TOK * 16 : 8];
+  __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int64_t N = p.N, SB = p.SB, M = p.M;
   const int64_t m0 = (int64_t)blockIdx.z * TOK;
-  const int64_t sb_begin = (int64_t)blockIdx.y * p.sps;
-  const int64_t sb_end = (sb_begin + p.sps < SB) ? sb_begin + p.sps : SB;
-  const int64_t nrow = (int64_t)blockIdx.x * NT + wv * 16 + r;
+  const int64_t s0 = (int64_t)blockIdx.y * p.sps;
+  const int64_t s1 = (s0 + p.sps < SB) ? s0 + p.sps : SB;
+  const int64_t nrow = (int64_t)blockIdx.x * ROWS + wv * 16 + r;
   const bool row_ok = nrow < N;
   // Buffer resources: loads past num_records read as zero (rows >= N,
-  // tokens >= M).  The host guarantees both buffers are below 2 GiB.
+  // tokens >= M).  The host keeps both operands below 2 GiB.
   const rsrc_t wr = make_rsrc(p.w, N * SB * BYTES);
   const rsrc_t xr = make_rsrc(p.xq, M * SB * Q8K_BYTES);
   const uint32_t wrow_off = (uint32_t)(nrow * SB * BYTES);
 
-  // Per-token power-of-two pre-scale (Q4_K: keeps the f16 halves of
-  // d_x * S_j in range); 1 for Q6_K.
+  // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
+  // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
   if (tid < TOK) {
     float esc = 1.0f;
-    if constexpr (QT == QT_Q4K) {
-      const int64_t m = m0 + tid;
+    if constexpr (MINS) {
       float mx = 0.0f;
-      if (m < M)
-        for (int64_t sb = sb_begin; sb < sb_end; ++sb)
-          mx = fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, buf_ld32(xr, (uint32_t)((m * SB + sb) * Q8K_BYTES)))));
+      for (int64_t sb = s0; sb < s1; ++sb)
+        mx = fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, buf_ld32(xr, (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES)))));
       if (mx > 0.0f) {
         int e = 0;
         (void)frexpf(mx, &e);
@@ -212,97 +215,100 @@ __global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
     }
     s_esc[tid] = esc;
   }
-  if constexpr (QT == QT_Q4K) {
-    for (int i = tid; i < 4 * TOK * 16; i += 256) s_amin[i] = (_Float16)0.0f;
+  if constexpr (MINS) {
+    for (int i = tid; i < 8 * TOK * 16; i += NTH) s_amin[i] = (_Float16)0.0f;
   }
+  __syncthreads();
+
+  // ---- activation staging: global -> registers (issued one super-block
+  // ahead) -> LDS.  Thread tid moves dword (tid & 63) of tokens wv + NW k.
+  const uint32_t act_step = (uint32_t)(NW * SB * Q8K_BYTES);
+  uint32_t av[STG];
+  uint32_t adx = 0;          // d_x bits (threads < TOK)
+  v4u abs0 = {}, abs1 = {};  // bsums (threads < TOK, Q4_K)
+  auto act_load = [&](int64_t sb) {
+    const uint32_t base = (uint32_t)(((m0 + wv) * SB + sb) * Q8K_BYTES) + 4 + 4 * (tid & 63);
+#pragma unroll
+    for (int k = 0; k < STG; ++k) av[k] = buf_ld32(xr, base + k * act_step);
+    if (tid < TOK) {
+      const uint32_t xoff = (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES);
+      adx = buf_ld32(xr, xoff);
+      if constexpr (MINS) {
+        abs0 = buf_ld128(xr, xoff + 260);
+        abs1 = buf_ld128(xr, xoff + 276);
+      }
+    }
+  };
+  auto act_store = [&](int buf, int slot8) {
+    uint8_t* dst = s_act[buf] + wv * ACT_STRIDE + 4 * (tid & 63);
+#pragma unroll
+    for (int k = 0; k < STG; ++k) *(uint32_t*)(dst + k * NW * ACT_STRIDE) = av[k];
+    if (tid < TOK) {
+      const float dx = __builtin_bit_cast(float, adx) * s_esc[tid];
+      s_dx[buf][tid] = dx;
+      if constexpr (MINS) {
+        // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1}),
+        // as f16 high and low halves
+        _Float16* dm = s_amin + (slot8 * TOK + tid) * 16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pr = (j < 4) ? abs0[j] : abs1[j - 4];
+          const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
+          const float a = dx * (float)S;
+          const _Float16 hi = (_Float16)a;
+          dm[j] = hi;
+          dm[8 + j] = (_Float16)(a - (float)hi);
+        }
+      }
+    }
+  };
 
   v4f yacc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) yacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  v8h bmin_hi = {}, bmin_lo = {};
+  v4u mhdr = {};  // Q4_K: header of block (group start + g4) for the min term
 
-  uint32_t raw[QTr<QT>::RAW];
-  load_raw<QT>(wr, wrow_off + (uint32_t)(sb_begin * BYTES), g4, raw);
+  // ---- prologue: weights for the first two super-blocks, first stage
+  uint32_t rawA[QTr<QT>::RAW], rawB[QTr<QT>::RAW];
+  load_raw<QT>(wr, wrow_off + (uint32_t)(s0 * BYTES), g4, rawA);
+  if (s0 + 1 < s1) load_raw<QT>(wr, wrow_off + (uint32_t)((s0 + 1) * BYTES), g4, rawB);
+  act_load(s0);
+  act_store(0, 0);
+  __syncthreads();
 
-  for (int64_t sb = sb_begin; sb < sb_end; ++sb) {
-    uint32_t cur[QTr<QT>::RAW];
-#pragma unroll
-    for (int i = 0; i < QTr<QT>::RAW; ++i) cur[i] = raw[i];
-    if (sb + 1 < sb_end) load_raw<QT>(wr, wrow_off + (uint32_t)((sb + 1) * BYTES), g4, raw);
-    const int slot = (int)((sb - sb_begin) & 3);
-
-    __syncthreads();  // previous super-block's LDS reads are done
-    // ---- stage this super-block's activations (int8) and scales in LDS
-    {
-      // thread tid moves dword (tid & 63) of tokens (tid >> 6) + 4k
-      constexpr int PER = TOK / 4;
-      const uint32_t base = (uint32_t)(((m0 + (tid >> 6)) * SB + sb) * Q8K_BYTES) + 4 + 4 * (tid & 63);
-      const uint32_t step = (uint32_t)(4 * SB * Q8K_BYTES);
-      uint8_t* dst = s_act + (tid >> 6) * ACT_STRIDE + 4 * (tid & 63);
-      uint32_t v[PER];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) v[k] = buf_ld32(xr, base + k * step);
-#pragma unroll
-      for (int k = 0; k < PER; ++k) *(uint32_t*)(dst + 4 * k * ACT_STRIDE) = v[k];
-    }
-    if (tid < TOK) {
-      const uint32_t xoff = (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES);
-      const float dx = __builtin_bit_cast(float, buf_ld32(xr, xoff)) * s_esc[tid];
-      s_dx[tid] = dx;
-      if constexpr (QT == QT_Q4K) {
-        // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1}),
-        // split into f16 high and low halves.
-        _Float16* dst = s_amin + (slot * TOK + tid) * 16;
-        const v4u bs0 = buf_ld128(xr, xoff + 260), bs1 = buf_ld128(xr, xoff + 276);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pr = (j < 4) ? bs0[j] : bs1[j - 4];
-          const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
-          const float a = dx * (float)S;
-          const _Float16 hi = (_Float16)a;
-          dst[j] = hi;
-          dst[8 + j] = (_Float16)(a - (float)hi);
-        }
-      }
-    }
-    // ---- Q4_K: at the start of each group of four super-blocks, the weight
-    // side of the min term for super-block (group start + g4): -dmin * m_j.
-    if constexpr (QT == QT_Q4K) {
+  for (int64_t sb = s0; sb < s1; ++sb) {
+    const int it = (int)(sb - s0);
+    const int buf = it & 1, slot = it & 3;
+    const bool more = sb + 1 < s1;
+    if (more) act_load(sb + 1);
+    if constexpr (MINS) {
+      // weight side of the min term for super-block (group start + g4),
+      // loaded at the group start and consumed at its end
       if (slot == 0) {
         const int64_t sbm = sb + g4;
-        float bm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (row_ok && sbm < sb_end) {
-          const v4u hdr = buf_ld128(wr, wrow_off + (uint32_t)(sbm * BYTES));
-          uint32_t sc03, sc47, mn03, mn47;
-          q4k_scales(hdr[1], hdr[2], hdr[3], sc03, sc47, mn03, mn47);
-          const float ndmin = -f16_bits_to_f32(hdr[0] >> 16);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t mb = (j < 4) ? mn03 : mn47;
-            bm[j] = ndmin * (float)((mb >> (8 * (j & 3))) & 63u);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const _Float16 hi = (_Float16)bm[j];
-          bmin_hi[j] = hi;
-          bmin_lo[j] = (_Float16)(bm[j] - (float)hi);
-        }
+        mhdr = (row_ok && sbm < s1) ? buf_ld128(wr, wrow_off + (uint32_t)(sbm * BYTES)) : v4u{0u, 0u, 0u, 0u};
       }
     }
+    uint32_t cur[QTr<QT>::RAW];
+#pragma unroll
+    for (int i = 0; i < QTr<QT>::RAW; ++i) cur[i] = rawA[i];
+#pragma unroll
+    for (int i = 0; i < QTr<QT>::RAW; ++i) rawA[i] = rawB[i];
+    if (sb + 2 < s1) load_raw<QT>(wr, wrow_off + (uint32_t)((sb + 2) * BYTES), g4, rawB);
+
     v4i alo[4], ahi[4];
     const float drow = unpack<QT>(cur, g4, alo, ahi);
-    __syncthreads();  // activations staged
-
-    // ---- integer contraction on MFMA (two planes x four K chunks) and the
-    // super-block epilogue y += (d * d_x) * ((hi << shift) + lo), one token
-    // block at a time so only 8 accumulator registers are live.
     float dsel[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dsel[i] = __shfl(drow, 4 * g4 + i);
+
+    // ---- integer contraction on MFMA (two planes x four K chunks) and the
+    // super-block epilogue y += (d * d_x) * ((hi << shift) + lo), one token
+    // block at a time
+    const uint8_t* act = s_act[buf];
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      const uint8_t* arow = s_act + (t * 16 + r) * ACT_STRIDE;
+      const uint8_t* arow = act + (t * 16 + r) * ACT_STRIDE;
       v4i accl = v4i{0, 0, 0, 0}, acch = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -312,23 +318,32 @@ __global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
         accl = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[c], b, accl, 0, 0, 0);
         acch = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[c], b, acch, 0, 0, 0);
       }
-      const float dx = s_dx[t * 16 + r];
+      const float dx = s_dx[buf][t * 16 + r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = (acch[i] << SHIFT) + accl[i];
         yacc[t][i] += (float)a * (dsel[i] * dx);
       }
     }
-    // ---- Q4_K min term, once per four super-blocks (or at the range end)
-    if constexpr (QT == QT_Q4K) {
-      if (slot == 3 || sb + 1 == sb_end) {
-        if (slot != 3 && g4 > slot) {
-          bmin_hi = v8h{};
-          bmin_lo = v8h{};
+    // ---- Q4_K min term, once per group of four super-blocks (or at the end)
+    if constexpr (MINS) {
+      if (slot == 3 || !more) {
+        v8h bmin_hi, bmin_lo;
+        uint32_t sc03, sc47, mn03, mn47;
+        q4k_scales(mhdr[1], mhdr[2], mhdr[3], sc03, sc47, mn03, mn47);
+        const float ndmin = -f16_bits_to_f32(mhdr[0] >> 16);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t mb = (j < 4) ? mn03 : mn47;
+          const float bm = ndmin * (float)((mb >> (8 * (j & 3))) & 63u);
+          const _Float16 hi = (_Float16)bm;
+          bmin_hi[j] = hi;
+          bmin_lo[j] = (_Float16)(bm - (float)hi);
         }
+        const int gbase = (it & 4);  // ring slots of this group: gbase .. gbase + 3
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-          const _Float16* src = s_amin + (g4 * TOK + t * 16 + r) * 16;
+          const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * 16;
           const v8h ahv = *(const v8h*)src;
           const v8h alv = *(const v8h*)(src + 8);
           yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, ahv, yacc[t], 0, 0, 0);
@@ -337,16 +352,18 @@ __global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
         }
       }
     }
+    if (more) act_store(buf ^ 1, (it + 1) & 7);
+    __syncthreads();
   }
 
-  // ---- write out: lane holds rows n0 + 4 g4 + i (i < 4) of token t*16 + r
-  const int64_t nbase = (int64_t)blockIdx.x * NT + wv * 16 + 4 * g4;
+  // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
+  const int64_t nbase = (int64_t)blockIdx.x * ROWS + wv * 16 + 4 * g4;
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int64_t m = m0 + t * 16 + r;
     const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
-    v4f yv = yacc[t] * inv;
+    const v4f yv = yacc[t] * inv;
     yacc[t] = yv;
     if (m < M) {
       float* dst = outp + m * p.ldo + nbase;
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void k_qgemm(GemmParams p) {
       const int64_t m = m0 + tid;
       uint64_t best = s_key[tid];
 #pragma unroll
-      for (int k = 1; k < 4; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
+      for (int k = 1; k < NW; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
       if (m < M) p.keys[(int64_t)blockIdx.x * M + m] = best;
     }
   }
@@ -453,31 +470,36 @@ __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w,
 }
 
 // ---- host-side launch helpers -------------------------------------------
-template <int QT, int TB, bool ARGMAX>
-static hipError_t launch_tb(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_qgemm<QT, TB, ARGMAX>), grid, dim3(256), 0, s, p);
+template <int QT, int TB, int NW, bool ARGMAX>
+static hipError_t launch_k(const GemmParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, ARGMAX>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-template <int QT, bool ARGMAX>
+template <int QT, int NW, bool ARGMAX>
 static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s) {
   switch (tb) {
-    case 1: return launch_tb<QT, 1, ARGMAX>(p, grid, s);
-    case 2: return launch_tb<QT, 2, ARGMAX>(p, grid, s);
-    case 3: return launch_tb<QT, 3, ARGMAX>(p, grid, s);
-    case 4: return launch_tb<QT, 4, ARGMAX>(p, grid, s);
-    case 5: return launch_tb<QT, 5, ARGMAX>(p, grid, s);
-    case 6: return launch_tb<QT, 6, ARGMAX>(p, grid, s);
-    case 7: return launch_tb<QT, 7, ARGMAX>(p, grid, s);
-    case 8: return launch_tb<QT, 8, ARGMAX>(p, grid, s);
-    case 9: return launch_tb<QT, 9, ARGMAX>(p, grid, s);
-    default: return launch_tb<QT, 10, ARGMAX>(p, grid, s);
+    case 1: return launch_k<QT, 1, NW, ARGMAX>(p, grid, s);
+    case 2: return launch_k<QT, 2, NW, ARGMAX>(p, grid, s);
+    case 3: return launch_k<QT, 3, NW, ARGMAX>(p, grid, s);
+    case 4: return launch_k<QT, 4, NW, ARGMAX>(p, grid, s);
+    case 5: return launch_k<QT, 5, NW, ARGMAX>(p, grid, s);
+    case 6: return launch_k<QT, 6, NW, ARGMAX>(p, grid, s);
+    case 7: return launch_k<QT, 7, NW, ARGMAX>(p, grid, s);
+    case 8: return launch_k<QT, 8, NW, ARGMAX>(p, grid, s);
+    case 9: return launch_k<QT, 9, NW, ARGMAX>(p, grid, s);
+    default: return launch_k<QT, 10, NW, ARGMAX>(p, grid, s);
   }
 }
 
-hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, dim3 grid, bool argmax, hipStream_t s) {
-  if (qtype == QT_Q4K) return argmax ? launch_q<QT_Q4K, true>(p, tb, grid, s) : launch_q<QT_Q4K, false>(p, tb, grid, s);
-  return argmax ? launch_q<QT_Q6K, true>(p, tb, grid, s) : launch_q<QT_Q6K, false>(p, tb, grid, s);
+// nw: waves per work-group (4 or 8): the tile is 16 * nw weight rows.
+hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int nw, dim3 grid, bool argmax, hipStream_t s) {
+  if (qtype == QT_Q4K) {
+    if (argmax) return launch_q<QT_Q4K, 4, true>(p, tb, grid, s);
+    return nw == 8 ? launch_q<QT_Q4K, 8, false>(p, tb, grid, s) : launch_q<QT_Q4K, 4, false>(p, tb, grid, s);
+  }
+  if (argmax) return launch_q<QT_Q6K, 4, true>(p, tb, grid, s);
+  return nw == 8 ? launch_q<QT_Q6K, 8, false>(p, tb, grid, s) : launch_q<QT_Q6K, 4, false>(p, tb, grid, s);
 }
 
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
