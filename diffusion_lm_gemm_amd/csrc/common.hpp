@@ -61,6 +61,19 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits16 & 0xFFFFu));
 }
 
+// Split an f32 into f16 halves with hi + lo == a to ~22 bits.  hi keeps the
+// top 11 significant bits of a by truncation (exact in f16 for |a| in the
+// normal f16 range), and lo is formed from exactly the bits stored in hi:
+// the compiler may lower separate f32->f16 conversions with different
+// rounding, so hi's value is pinned before it is reused.
+__device__ __forceinline__ void split_f16(float a, _Float16& hi, _Float16& lo) {
+  const float ht = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u);
+  unsigned short hb = __builtin_bit_cast(unsigned short, (_Float16)ht);
+  asm volatile("" : "+v"(hb));
+  hi = __builtin_bit_cast(_Float16, hb);
+  lo = (_Float16)(a - (float)hi);
+}
+
 // Dword at byte address p where p is 2-byte aligned (Q6_K blocks are 210 B,
 // so odd blocks start 2 bytes past a dword boundary).  Only dwords holding a
 // requested byte are read, so the read never leaves the block.

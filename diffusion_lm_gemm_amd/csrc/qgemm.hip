@@ -254,10 +254,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
         for (int j = 0; j < 8; ++j) {
           const uint32_t pr = (j < 4) ? abs0[j] : abs1[j - 4];
           const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
-          const float a = dx * (float)S;
-          const _Float16 hi = (_Float16)a;
-          dm[j] = hi;
-          dm[8 + j] = (_Float16)(a - (float)hi);
+          split_f16(dx * (float)S, dm[j], dm[8 + j]);
         }
       }
     }
@@ -335,10 +332,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t mb = (j < 4) ? mn03 : mn47;
-          const float bm = ndmin * (float)((mb >> (8 * (j & 3))) & 63u);
-          const _Float16 hi = (_Float16)bm;
+          _Float16 hi, lo;
+          split_f16(ndmin * (float)((mb >> (8 * (j & 3))) & 63u), hi, lo);
           bmin_hi[j] = hi;
-          bmin_lo[j] = (_Float16)(bm - (float)hi);
+          bmin_lo[j] = lo;
         }
         const int gbase = (it & 4);  // ring slots of this group: gbase .. gbase + 3
 #pragma unroll
