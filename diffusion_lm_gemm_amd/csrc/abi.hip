@@ -5,6 +5,7 @@
 // error-handling sections).
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/dllm.h"
 #include "common.hpp"
@@ -98,27 +99,43 @@ constexpr int64_t kCUs = 256;  // MI355X compute units
 
 struct Plan {
   int tb;
-  int nw;   // waves per work-group: tile = 16 * nw weight rows
+  int cfg;  // tile configuration (rows per work-group: qgemm_cfg_rows(cfg))
   int64_t n_tiles, m_tiles;
   int S;    // K splits
   int sps;  // super-blocks per split
 };
 
-// Pick the tile height (64 or 128 rows) and the K split that minimise an
-// estimate of the makespan: work-group rounds over the CUs (one work-group
-// per CU at a time) times super-blocks per work-group, plus a charge for
-// writing and re-reading split partials.  With no workspace, S = 1.
-Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
+// Time of one super-block step of a work-group at 160 tokens, per tile
+// configuration, in microseconds (fitted to measured single-GEMM times on
+// MI355X; the 4-wave 128-row tile runs one wave per SIMD and is slowest).
+constexpr double kCfgStepUs[3] = {6.5, 2.04, 2.4};
+
+// DLLM_QGEMM_TILE=0|1|2 pins the tile configuration (for testing every
+// configuration on any shape); unset, the planner chooses.
+static int forced_cfg() {
+  const char* e = getenv("DLLM_QGEMM_TILE");
+  if (!e || e[0] < '0' || e[0] > '2' || e[1]) return -1;
+  return e[0] - '0';
+}
+
+// Pick the tile configuration and the K split that minimise an estimate of
+// the makespan: work-group rounds over the CUs (one work-group per CU at a
+// time) times super-blocks per work-group, plus, for a split, the reduction
+// launch (~3 us) and moving S partial tiles of M x N f32 at ~4 TB/s.
+// With no workspace, S = 1.
+Plan plan_gemm(int /*qtype*/, int64_t N, int64_t K, int64_t M, bool allow_split) {
   Plan best{};
   double best_cost = 1e300;
   const int64_t SB = K / 256;
-  for (int nw : {8, 4}) {
-    // Q6_K at more than 128 tokens does not fit 8 waves' registers without spills
-    if (nw == 8 && qtype == DLLM_Q6_K && tb_for(M) >= 9) continue;
-    const int64_t rows = 16 * nw;
+  const int fc = forced_cfg();
+  for (int cfg : {2, 1, 0}) {
+    if (fc >= 0 && cfg != fc) continue;
+    const int64_t rows = qgemm_cfg_rows(cfg);
     const int64_t n_tiles = cdiv(N, rows);
     const int tb = tb_for(M);
     const int64_t m_tiles = cdiv(M, 16 * tb);
+    // per-step time scales roughly with the tokens per work-group
+    const double step_us = kCfgStepUs[cfg] * (0.25 + 0.75 * (double)(16 * tb) / 160.0);
     const int64_t smax = allow_split ? (SB < 16 ? SB : 16) : 1;
     for (int64_t S = 1; S <= smax; ++S) {
       const int64_t sps = cdiv(SB, S);
@@ -126,14 +143,11 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
       if (s_eff != S) continue;
       const int64_t wgs = n_tiles * m_tiles * S;
       const int64_t rounds = cdiv(wgs, kCUs);
-      // unit: one super-block of a 64-row tile (~0.65 us); 128 rows cost 2.
-      // +1.5 for filling the pipeline; a split adds the reduction launch
-      // (~3 us) and moving S partial tiles of M x N f32 at ~4 TB/s.
-      double cost = (double)rounds * (double)sps * (rows / 64.0) + 1.5;
-      if (S > 1) cost += (3e-6 + (double)S * (double)M * (double)N * 4.0 / 4e12) / 0.65e-6;
+      double cost = (double)rounds * (double)sps * step_us;
+      if (S > 1) cost += 3.0 + (double)S * (double)M * (double)N * 4.0 / 4e6;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
-        best = Plan{tb, nw, n_tiles, m_tiles, (int)S, (int)sps};
+        best = Plan{tb, cfg, n_tiles, m_tiles, (int)S, (int)sps};
       }
     }
   }
@@ -215,13 +229,13 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
     p.out = y;
     p.ldo = ldy;
     p.split_stride = 0;
-    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.nw, grid, false, s), "dllm_qgemm launch"))) return rc;
+    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), "dllm_qgemm launch"))) return rc;
     return ok();
   }
   p.out = (float*)workspace;
   p.ldo = N;
   p.split_stride = M * N;
-  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.nw, grid, false, s), "dllm_qgemm launch"))) return rc;
+  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), "dllm_qgemm launch"))) return rc;
   return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, s), "dllm_qgemm reduce launch");
 }
 
@@ -278,7 +292,7 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   const int tb = tb_for(n_rows);
   const int64_t n_tiles = cdiv(N, 64);  // 4 waves, 64 rows per work-group
   const dim3 grid((unsigned)n_tiles, 1, (unsigned)cdiv(n_rows, 16 * tb));
-  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 4, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
+  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 1, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
   return hip_status(launch_argmax_finalize(keys, n_tiles, n_rows, argmax, s), "dllm_lmhead_masked argmax launch");
 }
 

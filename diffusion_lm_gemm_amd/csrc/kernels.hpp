@@ -20,7 +20,10 @@ struct GemmParams {
 hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
                                hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
-hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int nw, dim3 grid, bool argmax, hipStream_t s);
+// cfg: tile configuration (0: 128 rows, 4 waves x 32 rows; 1: 64 rows, 4 waves
+// x 16 rows; 2: 128 rows, 8 waves x 16 rows).  argmax forces cfg 1.
+int qgemm_cfg_rows(int cfg);
+hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s);
 hipError_t launch_partials(int qtype, const uint8_t* w, int64_t N, int64_t SB, const uint8_t* xq, int64_t M,

@@ -149,15 +149,25 @@ __device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int
   }
 }
 
-// LDS byte offsets (within a token row) of the two 8-byte activation pieces
-// that pair with chunk c of lane group g4 (same K order as the A fragment).
+// LDS layout of one token's 256 activation bytes: the 16 bytes that pair
+// with lane group g4 of K chunk c (in the A fragment's K order) sit together
+// at byte 16 (4c + g4), so each B fragment is one 16-byte LDS read.  With a
+// 272-byte token stride the 16-byte reads of a wave fall in distinct banks.
+// act_dst maps the natural byte offset o (a multiple of 4) to that layout.
 template <int QT>
-__device__ __forceinline__ int act_off0(int c, int g4) {
-  return (QT == QT_Q4K) ? 64 * c + 8 * g4 : 128 * (c >> 1) + 32 * (c & 1) + 8 * g4;
-}
-template <int QT>
-__device__ __forceinline__ int act_off1(int c, int g4) {
-  return act_off0<QT>(c, g4) + ((QT == QT_Q4K) ? 32 : 64);
+__device__ __forceinline__ int act_dst(int o) {
+  int c, piece, l;
+  if constexpr (QT == QT_Q4K) {  // chunk c = bytes 64c..64c+63: two 32-byte pieces
+    c = o >> 6;
+    piece = (o >> 5) & 1;
+    l = o & 31;
+  } else {  // chunk c = (half h, quarter k & 1); piece = k >> 1
+    const int h = o >> 7, k = (o >> 5) & 3;
+    c = 2 * h + (k & 1);
+    piece = k >> 1;
+    l = o & 31;
+  }
+  return (4 * c + (l >> 3)) * 16 + piece * 8 + (l & 7);
 }
 
 __device__ __forceinline__ uint32_t f32_order_bits(float v) {
@@ -166,22 +176,32 @@ __device__ __forceinline__ uint32_t f32_order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int QT, int TB, int NW, bool ARGMAX>
+// NW waves per work-group, RB row blocks of 16 weight rows per wave: the tile
+// is 16 * RB * NW rows x 16 * TB tokens.  Each B fragment read from LDS feeds
+// 2 * RB MFMAs, so RB = 2 halves the LDS traffic per MFMA.
+template <int QT, int TB, int NW, int RB, bool ARGMAX>
 __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
   constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
   constexpr int NTH = 64 * NW;          // threads
-  constexpr int ROWS = 16 * NW;         // weight rows per work-group
+  constexpr int ROWS = 16 * RB * NW;    // weight rows per work-group
   constexpr int STG = TOK / NW;         // activation dwords per thread per stage
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
+  constexpr int RAW = QTr<QT>::RAW;
   constexpr bool MINS = (QT == QT_Q4K);
   // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
   // ring (two groups of four super-blocks) of min-term activation operands
   // [slot][token][hi8 | lo8] f16: one group is read while the next is written.
   __shared__ __attribute__((aligned(16))) uint8_t s_act[2][TOK * ACT_STRIDE];
-  __shared__ float s_dx[2][TOK];
+  // d_x staging: item i (a token, or a (token, j) pair for Q4_K) writes
+  // slot i, so every store has its own address; token t's value is read at
+  // item t * DXS.  Items past the end write the tail, which nothing reads.
+  constexpr int NITEM = MINS ? TOK * 8 : TOK;
+  constexpr int IPT = (NITEM + NTH - 1) / NTH;  // items per thread
+  constexpr int DXS = MINS ? 8 : 1;
+  __shared__ float s_dx[2][IPT * NTH];
   __shared__ float s_esc[TOK];
-  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 8 * TOK * 16 : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 8 * TOK * 16 + 2 * (IPT * NTH - NITEM) + 8 : 8];
   __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -190,22 +210,35 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
   const int64_t m0 = (int64_t)blockIdx.z * TOK;
   const int64_t s0 = (int64_t)blockIdx.y * p.sps;
   const int64_t s1 = (s0 + p.sps < SB) ? s0 + p.sps : SB;
-  const int64_t nrow = (int64_t)blockIdx.x * ROWS + wv * 16 + r;
-  const bool row_ok = nrow < N;
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS + wv * 16 * RB;  // first row of this wave
   // Buffer resources: loads past num_records read as zero (rows >= N,
   // tokens >= M).  The host keeps both operands below 2 GiB.
   const rsrc_t wr = make_rsrc(p.w, N * SB * BYTES);
   const rsrc_t xr = make_rsrc(p.xq, M * SB * Q8K_BYTES);
-  const uint32_t wrow_off = (uint32_t)(nrow * SB * BYTES);
+  uint32_t wrow_off[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int64_t nrow = row0 + 16 * b + r;  // the row this lane unpacks
+    row_ok[b] = nrow < N;
+    wrow_off[b] = (uint32_t)(nrow * SB * BYTES);
+  }
 
   // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
   // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
   if (tid < TOK) {
     float esc = 1.0f;
     if constexpr (MINS) {
+      // eight independent loads in flight per round
       float mx = 0.0f;
-      for (int64_t sb = s0; sb < s1; ++sb)
-        mx = fmaxf(mx, __builtin_fabsf(__builtin_bit_cast(float, buf_ld32(xr, (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES)))));
+      const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
+      for (int64_t sb = s0; sb < s1; sb += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mx = (sb + u < s1) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
+      }
       if (mx > 0.0f) {
         int e = 0;
         (void)frexpf(mx, &e);
@@ -221,121 +254,160 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
   __syncthreads();
 
   // ---- activation staging: global -> registers (issued one super-block
-  // ahead) -> LDS.  Thread tid moves dword (tid & 63) of tokens wv + NW k.
+  // ahead) -> LDS.  Thread tid moves dword (tid & 63) of tokens wv + NW k,
+  // placing it by act_dst.  d_x (and for Q4_K the min-term operands, one
+  // (token, j) pair per item) are spread over all threads.  Every load is
+  // unconditional -- past the end of the operand the buffer reads zero -- and
+  // so is every store (to its own LDS address): a fixed load count keeps the
+  // wait counts exact, and no branch lets the compiler sink the loads next to
+  // their use at the end of the iteration.
   const uint32_t act_step = (uint32_t)(NW * SB * Q8K_BYTES);
+  const int dcol = tid & 63;
+  const int dst_col = act_dst<QT>(4 * dcol);
   uint32_t av[STG];
-  uint32_t adx = 0;          // d_x bits (threads < TOK)
-  v4u abs0 = {}, abs1 = {};  // bsums (threads < TOK, Q4_K)
+  uint32_t idx_d[IPT], idx_b[IPT];
   auto act_load = [&](int64_t sb) {
-    const uint32_t base = (uint32_t)(((m0 + wv) * SB + sb) * Q8K_BYTES) + 4 + 4 * (tid & 63);
+    const uint32_t base = (uint32_t)(((m0 + wv) * SB + sb) * Q8K_BYTES) + 4 + 4 * dcol;
 #pragma unroll
-    for (int k = 0; k < STG; ++k) av[k] = buf_ld32(xr, base + k * act_step);
-    if (tid < TOK) {
-      const uint32_t xoff = (uint32_t)(((m0 + tid) * SB + sb) * Q8K_BYTES);
-      adx = buf_ld32(xr, xoff);
-      if constexpr (MINS) {
-        abs0 = buf_ld128(xr, xoff + 260);
-        abs1 = buf_ld128(xr, xoff + 276);
-      }
+    for (int k = 0; k < STG; ++k) av[k] = buf_ld32s(xr, base, k * act_step);
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int item = tid + k * NTH;
+      const int it_c = item < NITEM ? item : NITEM - 1;
+      const int tok = MINS ? (it_c >> 3) : it_c;
+      const uint32_t xoff = (uint32_t)(((m0 + tok) * SB + sb) * Q8K_BYTES);
+      idx_d[k] = buf_ld32(xr, xoff);
+      if constexpr (MINS) idx_b[k] = buf_ld32(xr, xoff + 260 + 4 * (it_c & 7));
     }
   };
   auto act_store = [&](int buf, int slot8) {
-    uint8_t* dst = s_act[buf] + wv * ACT_STRIDE + 4 * (tid & 63);
+    uint8_t* dst = s_act[buf] + wv * ACT_STRIDE + dst_col;
 #pragma unroll
     for (int k = 0; k < STG; ++k) *(uint32_t*)(dst + k * NW * ACT_STRIDE) = av[k];
-    if (tid < TOK) {
-      const float dx = __builtin_bit_cast(float, adx) * s_esc[tid];
-      s_dx[buf][tid] = dx;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int item = tid + k * NTH;
+      const bool live = item < NITEM;
+      const int it_c = live ? item : NITEM - 1;
+      const int tok = MINS ? (it_c >> 3) : it_c;
+      const float dx = __builtin_bit_cast(float, idx_d[k]) * s_esc[tok];
+      s_dx[buf][item] = dx;
       if constexpr (MINS) {
         // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1}),
         // as f16 high and low halves
-        _Float16* dm = s_amin + (slot8 * TOK + tid) * 16;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pr = (j < 4) ? abs0[j] : abs1[j - 4];
-          const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
-          split_f16(dx * (float)S, dm[j], dm[8 + j]);
-        }
+        const int j = it_c & 7;
+        const uint32_t pr = idx_b[k];
+        const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
+        _Float16* dm_hi = s_amin + (live ? (slot8 * TOK + tok) * 16 + j : 8 * TOK * 16 + 2 * (item - NITEM));
+        _Float16* dm_lo = live ? dm_hi + 8 : dm_hi + 1;
+        split_f16(dx * (float)S, *dm_hi, *dm_lo);
       }
     }
   };
 
-  v4f yacc[TB];
+  v4f yacc[RB][TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) yacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4u mhdr = {};  // Q4_K: header of block (group start + g4) for the min term
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) yacc[b][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Q4_K: dmin and min bytes of block (group start + g4) of each row, taken
+  // from the lane's own block data when the loop passes that super-block
+  uint32_t mh0[RB], mh2[RB], mh3[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) mh0[b] = mh2[b] = mh3[b] = 0u;
 
-  // ---- prologue: weights for the first two super-blocks, first stage
-  uint32_t rawA[QTr<QT>::RAW], rawB[QTr<QT>::RAW];
-  load_raw<QT>(wr, wrow_off + (uint32_t)(s0 * BYTES), g4, rawA);
-  if (s0 + 1 < s1) load_raw<QT>(wr, wrow_off + (uint32_t)((s0 + 1) * BYTES), g4, rawB);
-  act_load(s0);
-  act_store(0, 0);
-  __syncthreads();
-
-  for (int64_t sb = s0; sb < s1; ++sb) {
+  // One super-block: stage the next activations, unpack this block's weights
+  // (loaded two super-blocks ago into `raw`, which is then refilled with the
+  // block two ahead), contract on MFMA, fold in the min term at the end of a
+  // group of four, publish the next stage.
+  auto step = [&](int64_t sb, uint32_t(&raw)[RB][RAW]) {
     const int it = (int)(sb - s0);
     const int buf = it & 1, slot = it & 3;
     const bool more = sb + 1 < s1;
-    if (more) act_load(sb + 1);
-    if constexpr (MINS) {
-      // weight side of the min term for super-block (group start + g4),
-      // loaded at the group start and consumed at its end
-      if (slot == 0) {
-        const int64_t sbm = sb + g4;
-        mhdr = (row_ok && sbm < s1) ? buf_ld128(wr, wrow_off + (uint32_t)(sbm * BYTES)) : v4u{0u, 0u, 0u, 0u};
+    act_load(sb + 1);
+    v4i alo[RB][4], ahi[RB][4];
+    float dsel[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const float drow = unpack<QT>(raw[b], g4, alo[b], ahi[b]);
+      if constexpr (MINS) {
+        const bool mine = (slot == g4);
+        mh0[b] = mine ? raw[b][0] : mh0[b];
+        mh2[b] = mine ? raw[b][2] : mh2[b];
+        mh3[b] = mine ? raw[b][3] : mh3[b];
       }
+      load_raw<QT>(wr, wrow_off[b] + (uint32_t)((sb + 2) * BYTES), g4, raw[b]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsel[b][i] = __shfl(drow, 4 * g4 + i);
     }
-    uint32_t cur[QTr<QT>::RAW];
-#pragma unroll
-    for (int i = 0; i < QTr<QT>::RAW; ++i) cur[i] = rawA[i];
-#pragma unroll
-    for (int i = 0; i < QTr<QT>::RAW; ++i) rawA[i] = rawB[i];
-    if (sb + 2 < s1) load_raw<QT>(wr, wrow_off + (uint32_t)((sb + 2) * BYTES), g4, rawB);
 
-    v4i alo[4], ahi[4];
-    const float drow = unpack<QT>(cur, g4, alo, ahi);
-    float dsel[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dsel[i] = __shfl(drow, 4 * g4 + i);
-
-    // ---- integer contraction on MFMA (two planes x four K chunks) and the
-    // super-block epilogue y += (d * d_x) * ((hi << shift) + lo), one token
-    // block at a time
+    // integer contraction (two planes x four K chunks x RB row blocks) and
+    // the super-block epilogue y += (d * d_x) * ((hi << shift) + lo),
+    // software-pipelined over the token blocks: the B fragments of block t+1
+    // are read while block t's MFMAs run, and block t-1's integer sums are
+    // folded into y meanwhile.
     const uint8_t* act = s_act[buf];
+    auto loadB = [&](int t, v4i(&dstB)[4]) {
+      const uint8_t* arow = act + (t * 16 + r) * ACT_STRIDE + g4 * 16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + 64 * c);
+    };
+    auto flush = [&](int t, const v4i(&al)[RB], const v4i(&ah)[RB]) {
+      const float dx = s_dx[buf][(t * 16 + r) * DXS];
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = (ah[b][i] << SHIFT) + al[b][i];
+          yacc[b][t][i] += (float)a * (dsel[b][i] * dx);
+        }
+    };
+    v4i Bc[4], Bn[4];
+    loadB(0, Bc);
+    v4i pl[RB], ph[RB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      const uint8_t* arow = act + (t * 16 + r) * ACT_STRIDE;
-      v4i accl = v4i{0, 0, 0, 0}, acch = v4i{0, 0, 0, 0};
+      if (t + 1 < TB) loadB(t + 1, Bn);
+      v4i al[RB], ah[RB];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint2 b0 = *(const uint2*)(arow + act_off0<QT>(c, g4));
-        const uint2 b1 = *(const uint2*)(arow + act_off1<QT>(c, g4));
-        const v4i b = v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y};
-        accl = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[c], b, accl, 0, 0, 0);
-        acch = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[c], b, acch, 0, 0, 0);
-      }
-      const float dx = s_dx[buf][t * 16 + r];
+      for (int b = 0; b < RB; ++b) al[b] = ah[b] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int a = (acch[i] << SHIFT) + accl[i];
-        yacc[t][i] += (float)a * (dsel[i] * dx);
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          al[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[b][c], Bc[c], al[b], 0, 0, 0);
+          ah[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[b][c], Bc[c], ah[b], 0, 0, 0);
+        }
+      if (t > 0) flush(t - 1, pl, ph);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        pl[b] = al[b];
+        ph[b] = ah[b];
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
     }
-    // ---- Q4_K min term, once per group of four super-blocks (or at the end)
+    flush(TB - 1, pl, ph);
+
+    // Q4_K min term, once per group of four super-blocks (or at the end);
+    // lanes whose super-block lies past the end contribute zero
     if constexpr (MINS) {
       if (slot == 3 || !more) {
-        v8h bmin_hi, bmin_lo;
-        uint32_t sc03, sc47, mn03, mn47;
-        q4k_scales(mhdr[1], mhdr[2], mhdr[3], sc03, sc47, mn03, mn47);
-        const float ndmin = -f16_bits_to_f32(mhdr[0] >> 16);
+        v8h bmin_hi[RB], bmin_lo[RB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t mb = (j < 4) ? mn03 : mn47;
-          _Float16 hi, lo;
-          split_f16(ndmin * (float)((mb >> (8 * (j & 3))) & 63u), hi, lo);
-          bmin_hi[j] = hi;
-          bmin_lo[j] = lo;
+        for (int b = 0; b < RB; ++b) {
+          const bool live = row_ok[b] && g4 <= slot;
+          uint32_t sc03, sc47, mn03, mn47;
+          q4k_scales(0u, live ? mh2[b] : 0u, live ? mh3[b] : 0u, sc03, sc47, mn03, mn47);
+          const float ndmin = -f16_bits_to_f32(live ? (mh0[b] >> 16) : 0u);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t mb = (j < 4) ? mn03 : mn47;
+            _Float16 hi, lo;
+            split_f16(ndmin * (float)((mb >> (8 * (j & 3))) & 63u), hi, lo);
+            bmin_hi[b][j] = hi;
+            bmin_lo[b][j] = lo;
+          }
         }
         const int gbase = (it & 4);  // ring slots of this group: gbase .. gbase + 3
 #pragma unroll
@@ -343,33 +415,57 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
           const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * 16;
           const v8h ahv = *(const v8h*)src;
           const v8h alv = *(const v8h*)(src + 8);
-          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, ahv, yacc[t], 0, 0, 0);
-          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, alv, yacc[t], 0, 0, 0);
-          yacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_lo, ahv, yacc[t], 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            yacc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi[b], ahv, yacc[b][t], 0, 0, 0);
+            yacc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi[b], alv, yacc[b][t], 0, 0, 0);
+            yacc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_lo[b], ahv, yacc[b][t], 0, 0, 0);
+          }
         }
       }
     }
-    if (more) act_store(buf ^ 1, (it + 1) & 7);
+    act_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
     __syncthreads();
+  };
+
+  // ---- prologue: weights for the first two super-blocks, first stage
+  uint32_t rawA[RB][RAW], rawB[RB][RAW];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, rawA[b]);
+    load_raw<QT>(wr, wrow_off[b] + (uint32_t)((s0 + 1) * BYTES), g4, rawB[b]);
   }
+  act_load(s0);
+  act_store(0, 0);
+  __syncthreads();
+
+  int64_t sb = s0;
+  for (; sb + 1 < s1; sb += 2) {
+    step(sb, rawA);
+    step(sb + 1, rawB);
+  }
+  if (sb < s1) step(sb, rawA);
 
   // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
-  const int64_t nbase = (int64_t)blockIdx.x * ROWS + wv * 16 + 4 * g4;
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
 #pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int64_t m = m0 + t * 16 + r;
-    const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
-    const v4f yv = yacc[t] * inv;
-    yacc[t] = yv;
-    if (m < M) {
-      float* dst = outp + m * p.ldo + nbase;
-      if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
-        *(v4f*)dst = yv;
-      } else {
+  for (int b = 0; b < RB; ++b) {
+    const int64_t nbase = row0 + 16 * b + 4 * g4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (nbase + i < N) dst[i] = yv[i];
+    for (int t = 0; t < TB; ++t) {
+      const int64_t m = m0 + t * 16 + r;
+      const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
+      const v4f yv = yacc[b][t] * inv;
+      yacc[b][t] = yv;
+      if (m < M) {
+        float* dst = outp + m * p.ldo + nbase;
+        if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
+          *(v4f*)dst = yv;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nbase + i < N) dst[i] = yv[i];
+        }
       }
     }
   }
@@ -380,13 +476,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
     for (int t = 0; t < TB; ++t) {
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = nbase + i;
-        if (n < N) {
-          const uint64_t key = ((uint64_t)f32_order_bits(yacc[t][i]) << 32) | (uint64_t)(~(uint32_t)n);
-          best = key > best ? key : best;
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t n = row0 + 16 * b + 4 * g4 + i;
+          if (n < N) {
+            const uint64_t key = ((uint64_t)f32_order_bits(yacc[b][t][i]) << 32) | (uint64_t)(~(uint32_t)n);
+            best = key > best ? key : best;
+          }
         }
-      }
       const uint64_t o1 = __shfl_xor(best, 16);
       best = o1 > best ? o1 : best;
       const uint64_t o2 = __shfl_xor(best, 32);
@@ -467,36 +565,44 @@ __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w,
 }
 
 // ---- host-side launch helpers -------------------------------------------
-template <int QT, int TB, int NW, bool ARGMAX>
+template <int QT, int TB, int NW, int RB, bool ARGMAX>
 static hipError_t launch_k(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, ARGMAX>), grid, dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-template <int QT, int NW, bool ARGMAX>
+template <int QT, int NW, int RB, bool ARGMAX>
 static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s) {
   switch (tb) {
-    case 1: return launch_k<QT, 1, NW, ARGMAX>(p, grid, s);
-    case 2: return launch_k<QT, 2, NW, ARGMAX>(p, grid, s);
-    case 3: return launch_k<QT, 3, NW, ARGMAX>(p, grid, s);
-    case 4: return launch_k<QT, 4, NW, ARGMAX>(p, grid, s);
-    case 5: return launch_k<QT, 5, NW, ARGMAX>(p, grid, s);
-    case 6: return launch_k<QT, 6, NW, ARGMAX>(p, grid, s);
-    case 7: return launch_k<QT, 7, NW, ARGMAX>(p, grid, s);
-    case 8: return launch_k<QT, 8, NW, ARGMAX>(p, grid, s);
-    case 9: return launch_k<QT, 9, NW, ARGMAX>(p, grid, s);
-    default: return launch_k<QT, 10, NW, ARGMAX>(p, grid, s);
+    case 1: return launch_k<QT, 1, NW, RB, ARGMAX>(p, grid, s);
+    case 2: return launch_k<QT, 2, NW, RB, ARGMAX>(p, grid, s);
+    case 3: return launch_k<QT, 3, NW, RB, ARGMAX>(p, grid, s);
+    case 4: return launch_k<QT, 4, NW, RB, ARGMAX>(p, grid, s);
+    case 5: return launch_k<QT, 5, NW, RB, ARGMAX>(p, grid, s);
+    case 6: return launch_k<QT, 6, NW, RB, ARGMAX>(p, grid, s);
+    case 7: return launch_k<QT, 7, NW, RB, ARGMAX>(p, grid, s);
+    case 8: return launch_k<QT, 8, NW, RB, ARGMAX>(p, grid, s);
+    case 9: return launch_k<QT, 9, NW, RB, ARGMAX>(p, grid, s);
+    default: return launch_k<QT, 10, NW, RB, ARGMAX>(p, grid, s);
   }
 }
 
-// nw: waves per work-group (4 or 8): the tile is 16 * nw weight rows.
-hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int nw, dim3 grid, bool argmax, hipStream_t s) {
-  if (qtype == QT_Q4K) {
-    if (argmax) return launch_q<QT_Q4K, 4, true>(p, tb, grid, s);
-    return nw == 8 ? launch_q<QT_Q4K, 8, false>(p, tb, grid, s) : launch_q<QT_Q4K, 4, false>(p, tb, grid, s);
-  }
-  if (argmax) return launch_q<QT_Q6K, 4, true>(p, tb, grid, s);
-  return nw == 8 ? launch_q<QT_Q6K, 8, false>(p, tb, grid, s) : launch_q<QT_Q6K, 4, false>(p, tb, grid, s);
+// Tile configurations: cfg 0 = 4 waves x 2 row blocks (128 rows, one wave per
+// SIMD), cfg 1 = 4 waves x 1 row block (64 rows), cfg 2 = 8 waves x 1 row
+// block (128 rows, two waves per SIMD).  The LM head (argmax) uses cfg 1.
+template <int QT>
+static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
+  if (argmax) return launch_q<QT, 4, 1, true>(p, tb, grid, s);
+  if (cfg == 0) return launch_q<QT, 4, 2, false>(p, tb, grid, s);
+  if (cfg == 1) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
+  return launch_q<QT, 8, 1, false>(p, tb, grid, s);
+}
+
+int qgemm_cfg_rows(int cfg) { return cfg == 1 ? 64 : 128; }
+
+hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
+  if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);
+  return launch_cfg<QT_Q6K>(p, tb, cfg, grid, argmax, s);
 }
 
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {

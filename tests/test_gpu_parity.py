@@ -146,6 +146,27 @@ def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
     assert_close_rows(y, ref, f"qgemm {qtype} {M}x{N}x{K} split={split}")
 
 
+@pytest.mark.parametrize("qtype", [12, 14])
+@pytest.mark.parametrize("tile", ["0", "1", "2"])
+@pytest.mark.parametrize("M,N,K", [(148, 333, 2048), (37, 130, 1024), (160, 256, 512)])
+def test_qgemm_every_tile_configuration(dl, monkeypatch, qtype, tile, M, N, K):
+    """Each work-group shape (128 rows as 4 waves x 32 or 8 waves x 16, and
+    64 rows as 4 waves x 16), pinned through DLLM_QGEMM_TILE, on ragged rows
+    and tokens, split and unsplit."""
+    monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
+    _say(f"qgemm tile={tile} qtype={qtype} M={M} N={N} K={K}")
+    w = _weights(qtype, N, K, 11, f"t-{N}-{K}")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 11, f"tx-{M}-{K}").numpy())
+    ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
+    nb = max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    xd = torch.from_numpy(xq).to(DEV)
+    wd = w.to(DEV)
+    for workspace in (ws, None):
+        y = dl.qgemm(qtype, wd, N, K, xd, M, workspace=workspace).cpu().numpy()
+        assert_close_rows(y, ref, f"qgemm tile {tile} {qtype} {M}x{N}x{K} ws={workspace is not None}")
+
+
 @pytest.mark.parametrize("qtype,N,K", [(12, 4096, 4096), (14, 4096, 12288)])
 def test_qgemm_full_size_layers(dl, qtype, N, K):
     """Single LLaDA-8B linear layers at L = 148: attn_q (Q4_K 4096x4096) and
