@@ -103,7 +103,7 @@ def main():
     ws_bytes = max(dl.qgemm_workspace_bytes(q, n, k, L) for q, n, k in
                    [(Q4, 3 * D, D), (Q4, 2 * D, D), (Q6, D, D), (Q4, D, D), (Q4, 2 * FFN, D),
                     (Q4, D, FFN), (Q6, D, FFN)])
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     ws_lm = torch.empty(dl.lmhead_workspace_bytes(Q6, VOCAB, D, MASKED), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup

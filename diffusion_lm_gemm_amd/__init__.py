@@ -123,6 +123,13 @@ def qgemm_workspace_bytes(qtype: int, N: int, K: int, M: int) -> int:
     return int(lib.dllm_qgemm_workspace_bytes(qtype, N, K, M))
 
 
+def qgemm_workspace(qtype: int, N: int, K: int, M: int, device) -> torch.Tensor:
+    """A workspace for dllm_qgemm's K split at this shape (at least 256
+    bytes, zero-filled)."""
+    nb = max(qgemm_workspace_bytes(qtype, N, K, M), 256)
+    return torch.zeros(nb, dtype=torch.uint8, device=device)
+
+
 def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: int,
           y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y[M, N] (f32) = dequant(x_q8k) @ dequant(w)^T.  `y` may be a row-strided

@@ -105,37 +105,39 @@ struct Plan {
   int sps;  // super-blocks per split
 };
 
-// Time of one super-block step of a work-group at 160 tokens, per tile
-// configuration, in microseconds (fitted to measured single-GEMM times on
-// MI355X; the 4-wave 128-row tile runs one wave per SIMD and is slowest).
-constexpr double kCfgStepUs[3] = {6.5, 2.04, 2.4};
+// Time of one super-block step of a work-group with a full token tile, per
+// tile configuration, in microseconds, and its factor for Q6_K (heavier
+// unpacking), fitted to measured single-GEMM times on MI355X at 148 tokens.
+constexpr double kCfgStepUs[5] = {0.0, 2.709, 2.736, 2.785, 1.739};
+constexpr double kCfgQ6Factor[5] = {0.0, 1.060, 1.379, 1.735, 1.819};
 
-// DLLM_QGEMM_TILE=0|1|2 pins the tile configuration (for testing every
+// DLLM_QGEMM_TILE=1|2|3|4 pins the tile configuration (for testing every
 // configuration on any shape); unset, the planner chooses.
 static int forced_cfg() {
   const char* e = getenv("DLLM_QGEMM_TILE");
-  if (!e || e[0] < '0' || e[0] > '2' || e[1]) return -1;
+  if (!e || e[0] < '1' || e[0] > '4' || e[1]) return -1;
   return e[0] - '0';
 }
 
 // Pick the tile configuration and the K split that minimise an estimate of
-// the makespan: work-group rounds over the CUs (one work-group per CU at a
-// time) times super-blocks per work-group, plus, for a split, the reduction
-// launch (~3 us) and moving S partial tiles of M x N f32 at ~4 TB/s.
-// With no workspace, S = 1.
-Plan plan_gemm(int /*qtype*/, int64_t N, int64_t K, int64_t M, bool allow_split) {
+// the makespan: work-group rounds over the CUs times super-blocks per
+// work-group times the step time, plus, for a split, the reduction (~2.4 us
+// and ~0.54 us per MB of partials).  With no workspace, S = 1.
+Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   Plan best{};
   double best_cost = 1e300;
   const int64_t SB = K / 256;
   const int fc = forced_cfg();
-  for (int cfg : {2, 1, 0}) {
+  for (int cfg : {4, 3, 2, 1}) {
     if (fc >= 0 && cfg != fc) continue;
     const int64_t rows = qgemm_cfg_rows(cfg);
     const int64_t n_tiles = cdiv(N, rows);
-    const int tb = tb_for(M);
+    const int max_tb = qgemm_cfg_max_tb(cfg);
+    const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
     const int64_t m_tiles = cdiv(M, 16 * tb);
     // per-step time scales roughly with the tokens per work-group
-    const double step_us = kCfgStepUs[cfg] * (0.25 + 0.75 * (double)(16 * tb) / 160.0);
+    const double step_us = kCfgStepUs[cfg] * (qtype == 14 ? kCfgQ6Factor[cfg] : 1.0) *
+                           (0.25 + 0.75 * (double)tb / (double)max_tb);
     const int64_t smax = allow_split ? (SB < 16 ? SB : 16) : 1;
     for (int64_t S = 1; S <= smax; ++S) {
       const int64_t sps = cdiv(SB, S);
@@ -144,7 +146,7 @@ Plan plan_gemm(int /*qtype*/, int64_t N, int64_t K, int64_t M, bool allow_split)
       const int64_t wgs = n_tiles * m_tiles * S;
       const int64_t rounds = cdiv(wgs, kCUs);
       double cost = (double)rounds * (double)sps * step_us;
-      if (S > 1) cost += 3.0 + (double)S * (double)M * (double)N * 4.0 / 4e6;
+      if (S > 1) cost += 2.4 + (double)S * (double)M * (double)N * 4.0 * 0.54e-6;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = Plan{tb, cfg, n_tiles, m_tiles, (int)S, (int)sps};

@@ -20,9 +20,11 @@ struct GemmParams {
 hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
                                hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
-// cfg: tile configuration (0: 128 rows, 4 waves x 32 rows; 1: 64 rows, 4 waves
-// x 16 rows; 2: 128 rows, 8 waves x 16 rows).  argmax forces cfg 1.
+// cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
+// 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up
+// to 80 tokens).  argmax forces cfg 1.
 int qgemm_cfg_rows(int cfg);
+int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s);

@@ -34,7 +34,13 @@
 
 namespace dllm {
 
-constexpr int ACT_STRIDE = 272;  // LDS bytes per token row (256 + 16: spreads banks)
+// LDS holds each token's 256 activation bytes in natural K order as sixteen
+// 16-byte units, unit u of token tok stored at unit slot u ^ (tok & 15): the
+// 16-byte B-fragment reads of 16 consecutive tokens then fall in 16 distinct
+// slots (no bank conflicts), and the rows stay dense, so buffer-to-LDS loads
+// (which write 16 bytes per lane to consecutive addresses) can fill them by
+// choosing which global unit each lane fetches.
+constexpr int ACT_ROW = 256;
 
 template <int QT>
 struct QTr;
@@ -48,13 +54,37 @@ template <>
 struct QTr<QT_Q6K> {
   static constexpr int BYTES = Q6K_BYTES;
   static constexpr int SHIFT = 7;
-  static constexpr int RAW = 17;
+  static constexpr int RAW = 26;
 };
-
-
 
 __device__ __forceinline__ uint32_t pkmul(uint32_t a, uint32_t b) {
   return as_u32(as_u16x2(a) * as_u16x2(b));
+}
+
+// K order of the MFMA fragments.  For K chunk c (0..3) of a super-block,
+// lane group g4 (lanes 16 g4 .. 16 g4 + 15) holds 16 consecutive K values,
+// activation unit act_unit<QT>(c, g4) (bytes 16 u .. 16 u + 15 of the block).
+// Chunks are chosen so that each lane unpacks them from bytes it loads itself,
+// with a nibble choice that is the same for every lane of a chunk:
+//   Q4_K: chunk c = (half h = c >> 1, nibble n = c & 1): the n-nibbles of
+//         quant bytes 64 h + 16 g4 .. + 15, i.e. sub-block 4h + 2(g4 >> 1) + n,
+//         positions 16 (g4 & 1) .. + 15.
+//   Q6_K: chunk c = (half h = c >> 1, nibble n = c & 1): low-bit bytes
+//         64 h + 16 g4 .. + 15 (nibble n) with high-bit bytes
+//         32 h + 16 (g4 & 1) .. + 15, i.e. quarter k = 2n + (g4 >> 1) of half h,
+//         positions 16 (g4 & 1) .. + 15.
+template <int QT>
+__device__ __forceinline__ int act_unit(int c, int g4) {
+  if constexpr (QT == QT_Q4K) return 8 * (c >> 1) + 4 * (g4 >> 1) + 2 * (c & 1) + (g4 & 1);
+  else return 8 * (c >> 1) + 4 * (c & 1) + g4;
+}
+
+// Five dwords at the dword-aligned byte offset a (16 bytes starting at a or
+// a + 2, see unpack).
+__device__ __forceinline__ void ld5(rsrc_t r, uint32_t a, uint32_t* d) {
+  const v4u v = buf_ld128(r, a);
+  d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+  d[4] = buf_ld32(r, a + 16);
 }
 
 // Raw (packed) bytes of the lane's part of one weight super-block at byte
@@ -63,28 +93,33 @@ __device__ __forceinline__ uint32_t pkmul(uint32_t a, uint32_t b) {
 template <int QT>
 __device__ __forceinline__ void load_raw(rsrc_t wr, uint32_t off, int g4, uint32_t (&raw)[QTr<QT>::RAW]) {
   if constexpr (QT == QT_Q4K) {
-    // header (d | dmin, 12 scale/min bytes) and, per chunk c, the 8 nibble
-    // bytes at 16 + 32c + 8 g4.
+    // header (d | dmin, 12 scale/min bytes), then quant bytes 16 g4 .. and
+    // 64 + 16 g4 .. of the 128-byte quant area.  Blocks are 144 bytes, so
+    // every piece is 16-byte aligned.
     const v4u hdr = buf_ld128(wr, off);
-    raw[0] = hdr[0]; raw[1] = hdr[1]; raw[2] = hdr[2]; raw[3] = hdr[3];
+    const v4u q0 = buf_ld128(wr, off + 16 + 16 * g4);
+    const v4u q1 = buf_ld128(wr, off + 16 + 64 + 16 * g4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const v2u v = buf_ld64(wr, off + 16 + 32 * c + 8 * g4);
-      raw[4 + 2 * c] = v[0];
-      raw[5 + 2 * c] = v[1];
+    for (int i = 0; i < 4; ++i) {
+      raw[i] = hdr[i];
+      raw[4 + i] = q0[i];
+      raw[8 + i] = q1[i];
     }
   } else {
-    // per chunk c = (half h, quarter pair k1): low-nibble bytes at
-    // 64h + 32k1 + 8 g4; per half: high-bit bytes at 128 + 32h + 8 g4;
-    // 16 scale bytes at 192; f16 d at 208.  Blocks are 210 bytes, so a block
-    // may start 2 bytes past a dword boundary.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) buf_ld64_a2(wr, off + 64 * (c >> 1) + 32 * (c & 1) + 8 * g4, raw[2 * c], raw[2 * c + 1]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) buf_ld64_a2(wr, off + 128 + 32 * h + 8 * g4, raw[8 + 2 * h], raw[9 + 2 * h]);
-    buf_ld64_a2(wr, off + 192, raw[12], raw[13]);
-    buf_ld64_a2(wr, off + 200, raw[14], raw[15]);
-    raw[16] = buf_ld16(wr, off + 208);
+    // Blocks are 210 bytes, so a block starts at a dword boundary or two
+    // bytes past one; each 16-byte field is fetched as the five dwords that
+    // cover it and aligned when unpacked.  Fields: low-bit bytes 64h + 16 g4
+    // (h = 0, 1), high-bit bytes 128 + 32h + 16 (g4 & 1), the 16 scales at
+    // 192, and the f16 d at 208 (a 16-bit load: a dword there would reach
+    // past the end of the buffer for a dword-aligned last block, and the
+    // buffer's range check would zero all of it).
+    const uint32_t a = off & ~3u;
+    ld5(wr, a + 16 * g4, raw);
+    ld5(wr, a + 64 + 16 * g4, raw + 5);
+    ld5(wr, a + 128 + 16 * (g4 & 1), raw + 10);
+    ld5(wr, a + 160 + 16 * (g4 & 1), raw + 15);
+    ld5(wr, a + 192, raw + 20);
+    raw[25] = buf_ld16(wr, off + 208);
   }
 }
 
@@ -100,74 +135,64 @@ __device__ __forceinline__ void q6_planes(uint32_t q, uint32_t s2, uint32_t c64,
   lo = __builtin_amdgcn_perm(wo, we, 0x06020400u) >> 1;
 }
 
-// Unpack raw bytes into the two int8 planes of the four 16x64 A fragments and
-// return the super-block factor d.
+// Unpack raw bytes into the two int8 planes of the four 16x64 A fragments
+// (K order of act_unit) and return the super-block factor d.  soff: the byte
+// offset of the block mod 4 (Q6_K only: 0 or 2).
 template <int QT>
-__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, v4i (&alo)[4], v4i (&ahi)[4]) {
+__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, uint32_t soff, v4i (&alo)[4],
+                                        v4i (&ahi)[4]) {
   if constexpr (QT == QT_Q4K) {
     uint32_t sc03, sc47, mn03, mn47;
     q4k_scales(raw[1], raw[2], raw[3], sc03, sc47, mn03, mn47);
-    const uint32_t sl03 = sc03 & 0x07070707u, sh03 = (sc03 >> 3) & 0x07070707u;
-    const uint32_t sl47 = sc47 & 0x07070707u, sh47 = (sc47 >> 3) & 0x07070707u;
+    const int jb0 = 2 * (g4 >> 1);  // sub-block byte of chunk (h, 0); chunk (h, 1) is the next one
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // sub-blocks 2c (low nibbles) and 2c+1 (high nibbles)
-      const uint32_t slv = (c < 2) ? sl03 : sl47, shv = (c < 2) ? sh03 : sh47;
-      const int je = (2 * c) & 3, jo = (2 * c + 1) & 3;
-      const uint32_t sle = splat_byte_u16x2(slv, je), slo = splat_byte_u16x2(slv, jo);
-      const uint32_t she = splat_byte_u16x2(shv, je), sho = splat_byte_u16x2(shv, jo);
-      const uint32_t v0 = raw[4 + 2 * c], v1 = raw[5 + 2 * c];
-      const uint32_t n0l = q4k_lo_nibbles(v0), n1l = q4k_lo_nibbles(v1);
-      const uint32_t n0h = q4k_hi_nibbles(v0), n1h = q4k_hi_nibbles(v1);
-      alo[c] = v4i{(int)pkmul(n0l, sle), (int)pkmul(n1l, sle), (int)pkmul(n0h, slo), (int)pkmul(n1h, slo)};
-      ahi[c] = v4i{(int)pkmul(n0l, she), (int)pkmul(n1l, she), (int)pkmul(n0h, sho), (int)pkmul(n1h, sho)};
-    }
-    return f16_bits_to_f32(raw[0]);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int h = c >> 1, k1 = c & 1;
-      // scale index g = i/16 for quarters k1 and k1+2 at l = 8 g4 .. 8 g4 + 7
-      const int gl = 8 * h + 2 * k1 + (g4 >> 1), gh = gl + 4;
-      const int sl = (int)(int8_t)(raw[12 + (gl >> 2)] >> (8 * (gl & 3)));
-      const int sh = (int)(int8_t)(raw[12 + (gh >> 2)] >> (8 * (gh & 3)));
-      const uint32_t s2l = ((uint32_t)(2 * sl) & 0xFFFFu) * 0x10001u;
-      const uint32_t c64l = ((uint32_t)(-64 * sl) & 0xFFFFu) * 0x10001u;
-      const uint32_t s2h = ((uint32_t)(2 * sh) & 0xFFFFu) * 0x10001u;
-      const uint32_t c64h = ((uint32_t)(-64 * sh) & 0xFFFFu) * 0x10001u;
-      const uint32_t L0 = raw[2 * c], L1 = raw[2 * c + 1];
-      const uint32_t H0 = raw[8 + 2 * h], H1 = raw[9 + 2 * h];
+      const int h = c >> 1, n = c & 1;
+      const uint32_t scv = h ? sc47 : sc03;
+      const uint32_t sl = splat_byte_u16x2(scv & 0x07070707u, jb0 + n);
+      const uint32_t sh = splat_byte_u16x2((scv >> 3) & 0x07070707u, jb0 + n);
       uint32_t lo[4], hi[4];
-      q6_planes(q6k_quants(L0, H0, k1), s2l, c64l, lo[0], hi[0]);
-      q6_planes(q6k_quants(L1, H1, k1), s2l, c64l, lo[1], hi[1]);
-      q6_planes(q6k_quants(L0, H0, k1 + 2), s2h, c64h, lo[2], hi[2]);
-      q6_planes(q6k_quants(L1, H1, k1 + 2), s2h, c64h, lo[3], hi[3]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t v = raw[4 + 4 * h + d];
+        const uint32_t nib = n ? q4k_hi_nibbles(v) : q4k_lo_nibbles(v);
+        lo[d] = pkmul(nib, sl);
+        hi[d] = pkmul(nib, sh);
+      }
       alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
       ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    return f16_bits_to_f32(raw[16]);
+    return f16_bits_to_f32(raw[0]);
+  } else {
+    uint32_t ql[2][4], qh[2][4], sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ql[0][i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], soff);
+      ql[1][i] = __builtin_amdgcn_alignbyte(raw[5 + i + 1], raw[5 + i], soff);
+      qh[0][i] = __builtin_amdgcn_alignbyte(raw[10 + i + 1], raw[10 + i], soff);
+      qh[1][i] = __builtin_amdgcn_alignbyte(raw[15 + i + 1], raw[15 + i], soff);
+      sc[i] = __builtin_amdgcn_alignbyte(raw[20 + i + 1], raw[20 + i], soff);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int h = c >> 1, n = c & 1;
+      // scale index 8h + 4n + g4: byte g4 of scale dword 2h + n
+      const int s = (int)(int8_t)(sc[2 * h + n] >> (8 * g4));
+      const uint32_t s2 = ((uint32_t)(2 * s) & 0xFFFFu) * 0x10001u;
+      const uint32_t c64 = ((uint32_t)(-64 * s) & 0xFFFFu) * 0x10001u;
+      const int hsh = 2 * (2 * n + (g4 >> 1));  // high bits of quarter k = 2n + (g4 >> 1)
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo4 = n ? q4k_hi_nibbles(ql[h][d]) : q4k_lo_nibbles(ql[h][d]);
+        const uint32_t hi2 = (qh[h][d] >> hsh) & 0x03030303u;
+        q6_planes(lo4 | (hi2 << 4), s2, c64, lo[d], hi[d]);
+      }
+      alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+      ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    return f16_bits_to_f32(raw[25]);
   }
-}
-
-// LDS layout of one token's 256 activation bytes: the 16 bytes that pair
-// with lane group g4 of K chunk c (in the A fragment's K order) sit together
-// at byte 16 (4c + g4), so each B fragment is one 16-byte LDS read.  With a
-// 272-byte token stride the 16-byte reads of a wave fall in distinct banks.
-// act_dst maps the natural byte offset o (a multiple of 4) to that layout.
-template <int QT>
-__device__ __forceinline__ int act_dst(int o) {
-  int c, piece, l;
-  if constexpr (QT == QT_Q4K) {  // chunk c = bytes 64c..64c+63: two 32-byte pieces
-    c = o >> 6;
-    piece = (o >> 5) & 1;
-    l = o & 31;
-  } else {  // chunk c = (half h, quarter k & 1); piece = k >> 1
-    const int h = o >> 7, k = (o >> 5) & 3;
-    c = 2 * h + (k & 1);
-    piece = k >> 1;
-    l = o & 31;
-  }
-  return (4 * c + (l >> 3)) * 16 + piece * 8 + (l & 7);
 }
 
 __device__ __forceinline__ uint32_t f32_order_bits(float v) {
@@ -178,30 +203,42 @@ __device__ __forceinline__ uint32_t f32_order_bits(float v) {
 
 // NW waves per work-group, RB row blocks of 16 weight rows per wave: the tile
 // is 16 * RB * NW rows x 16 * TB tokens.  Each B fragment read from LDS feeds
-// 2 * RB MFMAs, so RB = 2 halves the LDS traffic per MFMA.
+// 2 * RB MFMAs.
+// Four-wave tiles of at most 80 tokens fit two work-groups per CU (two waves
+// per SIMD, each with its own barrier); larger tiles run one per CU.
 template <int QT, int TB, int NW, int RB, bool ARGMAX>
-__global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
+__global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm(GemmParams p) {
   constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
   constexpr int NTH = 64 * NW;          // threads
   constexpr int ROWS = 16 * RB * NW;    // weight rows per work-group
-  constexpr int STG = TOK / NW;         // activation dwords per thread per stage
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
   constexpr int RAW = QTr<QT>::RAW;
   constexpr bool MINS = (QT == QT_Q4K);
+  // buffer-to-LDS loads per wave per stage: 16 units per token, 64 units per
+  // wave-wide load; the stage is padded to TOKP rows so the loads fill it
+  // exactly (the padding rows are loaded and never read).
+  constexpr int TOKP = (TOK + 4 * NW - 1) / (4 * NW) * (4 * NW);
+  constexpr int DPW = TOKP * 16 / (64 * NW);
   // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
-  // ring (two groups of four super-blocks) of min-term activation operands
-  // [slot][token][hi8 | lo8] f16: one group is read while the next is written.
-  __shared__ __attribute__((aligned(16))) uint8_t s_act[2][TOK * ACT_STRIDE];
-  // d_x staging: item i (a token, or a (token, j) pair for Q4_K) writes
-  // slot i, so every store has its own address; token t's value is read at
-  // item t * DXS.  Items past the end write the tail, which nothing reads.
-  constexpr int NITEM = MINS ? TOK * 8 : TOK;
+  // ring (two groups of four super-blocks) of min-term activation operands,
+  // high halves [slot][token][8] f16 then low halves likewise: one group is
+  // read while the next is written.  A lane's 16-byte read of one token's
+  // eight values has consecutive tokens at consecutive 16-byte slots, so the
+  // reads of a wave hit distinct banks.
+  __shared__ __attribute__((aligned(16))) uint8_t s_act[2][TOKP * ACT_ROW];
+  constexpr int AMS = 8;               // halves per token record of the ring
+  constexpr int AMLO = 8 * TOK * AMS;  // offset of the low halves
+  // d_x staging: items (a token, or for Q4_K a (token, half q) pair that
+  // covers sub-blocks 4q .. 4q+3) are spread over all threads.  Token t's d_x
+  // sits at slot t (written by its item with q = 0); every other item writes
+  // a slot of its own past TOK, which nothing reads, so every store is
+  // unconditional and has its own address.
+  constexpr int NITEM = MINS ? TOK * 2 : TOK;
   constexpr int IPT = (NITEM + NTH - 1) / NTH;  // items per thread
-  constexpr int DXS = MINS ? 8 : 1;
-  __shared__ float s_dx[2][IPT * NTH];
+  __shared__ float s_dx[2][TOK + IPT * NTH];
   __shared__ float s_esc[TOK];
-  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 8 * TOK * 16 + 2 * (IPT * NTH - NITEM) + 8 : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTH - NITEM) + 8 : 8];
   __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -224,83 +261,68 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
     wrow_off[b] = (uint32_t)(nrow * SB * BYTES);
   }
 
-  // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
-  // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
-  if (tid < TOK) {
-    float esc = 1.0f;
-    if constexpr (MINS) {
-      // eight independent loads in flight per round
-      float mx = 0.0f;
-      const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
-      for (int64_t sb = s0; sb < s1; sb += 8) {
-        float v[8];
+  // ---- activation staging.  The int8 quants go global -> LDS directly:
+  // load k of wave wv fills LDS units (wv DPW + k) 64 + lane, i.e. token
+  // u >> 4, slot u & 15, with global unit (slot ^ token) of that token's
+  // record (its quants start 4 bytes in).  d_x (and for Q4_K the min-term
+  // operands, one (token, j) pair per item) go through registers.  Every load
+  // is unconditional -- past the end of the operand the buffer reads zero --
+  // and so is every store (to its own LDS address).
+  const uint32_t dma_tok0 = (uint32_t)((m0 + wv * DPW * 4 + (lane >> 4)) * SB * Q8K_BYTES) + 4;
+  const uint32_t tok_step = (uint32_t)(4 * SB * Q8K_BYTES);
+  auto act_dma = [&](int buf, int64_t sb) {
+    const uint32_t soff = (uint32_t)(sb * Q8K_BYTES);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) mx = (sb + u < s1) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
-      }
-      if (mx > 0.0f) {
-        int e = 0;
-        (void)frexpf(mx, &e);
-        e = e < -100 ? -100 : (e > 100 ? 100 : e);
-        esc = ldexpf(1.0f, -e);
-      }
+    for (int k = 0; k < DPW; ++k) {
+      const int tok = (wv * DPW + k) * 4 + (lane >> 4);
+      const uint32_t voff = dma_tok0 + k * tok_step + 16 * ((lane & 15) ^ (tok & 15));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (__attribute__((address_space(3))) void*)(s_act[buf] + (wv * DPW + k) * 1024), 16, voff, soff, 0, 0);
     }
-    s_esc[tid] = esc;
-  }
-  if constexpr (MINS) {
-    for (int i = tid; i < 8 * TOK * 16; i += NTH) s_amin[i] = (_Float16)0.0f;
-  }
-  __syncthreads();
-
-  // ---- activation staging: global -> registers (issued one super-block
-  // ahead) -> LDS.  Thread tid moves dword (tid & 63) of tokens wv + NW k,
-  // placing it by act_dst.  d_x (and for Q4_K the min-term operands, one
-  // (token, j) pair per item) are spread over all threads.  Every load is
-  // unconditional -- past the end of the operand the buffer reads zero -- and
-  // so is every store (to its own LDS address): a fixed load count keeps the
-  // wait counts exact, and no branch lets the compiler sink the loads next to
-  // their use at the end of the iteration.
-  const uint32_t act_step = (uint32_t)(NW * SB * Q8K_BYTES);
-  const int dcol = tid & 63;
-  const int dst_col = act_dst<QT>(4 * dcol);
-  uint32_t av[STG];
-  uint32_t idx_d[IPT], idx_b[IPT];
-  auto act_load = [&](int64_t sb) {
-    const uint32_t base = (uint32_t)(((m0 + wv) * SB + sb) * Q8K_BYTES) + 4 + 4 * dcol;
-#pragma unroll
-    for (int k = 0; k < STG; ++k) av[k] = buf_ld32s(xr, base, k * act_step);
+  };
+  // idx_b: Q4_K bsum pairs (2j, 2j+1) for j = 4q .. 4q+3, one per dword
+  uint32_t idx_d[IPT];
+  v4u idx_b[MINS ? IPT : 1];
+  auto items_load = [&](int64_t sb) {
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int item = tid + k * NTH;
       const int it_c = item < NITEM ? item : NITEM - 1;
-      const int tok = MINS ? (it_c >> 3) : it_c;
+      const int tok = MINS ? (it_c >> 1) : it_c;
       const uint32_t xoff = (uint32_t)(((m0 + tok) * SB + sb) * Q8K_BYTES);
       idx_d[k] = buf_ld32(xr, xoff);
-      if constexpr (MINS) idx_b[k] = buf_ld32(xr, xoff + 260 + 4 * (it_c & 7));
+      if constexpr (MINS) idx_b[k] = buf_ld128(xr, xoff + 260 + 16 * (it_c & 1));
     }
   };
-  auto act_store = [&](int buf, int slot8) {
-    uint8_t* dst = s_act[buf] + wv * ACT_STRIDE + dst_col;
-#pragma unroll
-    for (int k = 0; k < STG; ++k) *(uint32_t*)(dst + k * NW * ACT_STRIDE) = av[k];
+  auto items_store = [&](int buf, int slot8) {
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int item = tid + k * NTH;
       const bool live = item < NITEM;
       const int it_c = live ? item : NITEM - 1;
-      const int tok = MINS ? (it_c >> 3) : it_c;
+      const int tok = MINS ? (it_c >> 1) : it_c;
       const float dx = __builtin_bit_cast(float, idx_d[k]) * s_esc[tok];
-      s_dx[buf][item] = dx;
+      if constexpr (!MINS) s_dx[buf][item] = dx;
       if constexpr (MINS) {
-        // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1}),
-        // as f16 high and low halves
-        const int j = it_c & 7;
-        const uint32_t pr = idx_b[k];
-        const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
-        _Float16* dm_hi = s_amin + (live ? (slot8 * TOK + tok) * 16 + j : 8 * TOK * 16 + 2 * (item - NITEM));
-        _Float16* dm_lo = live ? dm_hi + 8 : dm_hi + 1;
-        split_f16(dx * (float)S, *dm_hi, *dm_lo);
+        const int q = it_c & 1;
+        s_dx[buf][(live && q == 0) ? tok : TOK + item] = dx;
+        // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1})
+        // for j = 4q .. 4q+3, as f16 high and low halves
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        v4h hv, lv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t pr = idx_b[k][i];
+          const int S = (int)(int16_t)(pr & 0xFFFFu) + (int)(int16_t)(pr >> 16);
+          _Float16 h, l;
+          split_f16(dx * (float)S, h, l);
+          hv[i] = h;
+          lv[i] = l;
+        }
+        _Float16* dm_hi = s_amin + (live ? (slot8 * TOK + tok) * AMS + 4 * q : 2 * AMLO + 8 * (item - NITEM));
+        _Float16* dm_lo = live ? dm_hi + AMLO : dm_hi + 4;
+        *(v4h*)dm_hi = hv;
+        *(v4h*)dm_lo = lv;
       }
     }
   };
@@ -316,78 +338,80 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
 #pragma unroll
   for (int b = 0; b < RB; ++b) mh0[b] = mh2[b] = mh3[b] = 0u;
 
-  // One super-block: stage the next activations, unpack this block's weights
-  // (loaded two super-blocks ago into `raw`, which is then refilled with the
-  // block two ahead), contract on MFMA, fold in the min term at the end of a
-  // group of four, publish the next stage.
-  auto step = [&](int64_t sb, uint32_t(&raw)[RB][RAW]) {
+  // One super-block: start the next stage's loads, unpack this block's
+  // weights (loaded during the previous step into `raw`, which is then
+  // refilled with the next block), contract on MFMA, fold in the min term at
+  // the end of a group of four, publish the next stage's d_x.  The barrier at
+  // the end also waits for every load in flight.
+  uint32_t raw[RB][RAW];
+  auto step = [&](int64_t sb) {
     const int it = (int)(sb - s0);
     const int buf = it & 1, slot = it & 3;
     const bool more = sb + 1 < s1;
-    act_load(sb + 1);
+    act_dma(buf ^ 1, sb + 1);  // past the end: an unread stage
+    items_load(sb + 1);
     v4i alo[RB][4], ahi[RB][4];
     float dsel[RB][4];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const float drow = unpack<QT>(raw[b], g4, alo[b], ahi[b]);
+      const uint32_t boff = wrow_off[b] + (uint32_t)(sb * BYTES);
+      const float drow = unpack<QT>(raw[b], g4, boff & 3u, alo[b], ahi[b]);
       if constexpr (MINS) {
         const bool mine = (slot == g4);
         mh0[b] = mine ? raw[b][0] : mh0[b];
         mh2[b] = mine ? raw[b][2] : mh2[b];
         mh3[b] = mine ? raw[b][3] : mh3[b];
       }
-      load_raw<QT>(wr, wrow_off[b] + (uint32_t)((sb + 2) * BYTES), g4, raw[b]);
+      load_raw<QT>(wr, boff + BYTES, g4, raw[b]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dsel[b][i] = __shfl(drow, 4 * g4 + i);
     }
 
     // integer contraction (two planes x four K chunks x RB row blocks) and
     // the super-block epilogue y += (d * d_x) * ((hi << shift) + lo),
-    // software-pipelined over the token blocks: the B fragments of block t+1
-    // are read while block t's MFMAs run, and block t-1's integer sums are
-    // folded into y meanwhile.
+    // software-pipelined: the B fragments of token block t+1 are read while
+    // block t's MFMAs run, and each (token block, row block) tile's integer
+    // sums are folded into y while the next tile's MFMAs run.
     const uint8_t* act = s_act[buf];
+    int bunit[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bunit[c] = 16 * (act_unit<QT>(c, g4) ^ r);  // token t*16 + r has (tok & 15) == r
     auto loadB = [&](int t, v4i(&dstB)[4]) {
-      const uint8_t* arow = act + (t * 16 + r) * ACT_STRIDE + g4 * 16;
+      const uint8_t* arow = act + (t * 16 + r) * ACT_ROW;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + 64 * c);
+      for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + bunit[c]);
     };
-    auto flush = [&](int t, const v4i(&al)[RB], const v4i(&ah)[RB]) {
-      const float dx = s_dx[buf][(t * 16 + r) * DXS];
+    auto flush = [&](int t, int b, const v4i& al, const v4i& ah) {
+      const float dx = s_dx[buf][t * 16 + r];
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int a = (ah[b][i] << SHIFT) + al[b][i];
-          yacc[b][t][i] += (float)a * (dsel[b][i] * dx);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int a = (ah[i] << SHIFT) + al[i];
+        yacc[b][t][i] += (float)a * (dsel[b][i] * dx);
+      }
     };
     v4i Bc[4], Bn[4];
     loadB(0, Bc);
-    v4i pl[RB], ph[RB];
+    v4i pl = {0, 0, 0, 0}, ph = {0, 0, 0, 0};  // the tile waiting to be folded in
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       if (t + 1 < TB) loadB(t + 1, Bn);
-      v4i al[RB], ah[RB];
-#pragma unroll
-      for (int b = 0; b < RB; ++b) al[b] = ah[b] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          al[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[b][c], Bc[c], al[b], 0, 0, 0);
-          ah[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[b][c], Bc[c], ah[b], 0, 0, 0);
-        }
-      if (t > 0) flush(t - 1, pl, ph);
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
-        pl[b] = al[b];
-        ph[b] = ah[b];
+        v4i al = {0, 0, 0, 0}, ah = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          al = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo[b][c], Bc[c], al, 0, 0, 0);
+          ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi[b][c], Bc[c], ah, 0, 0, 0);
+        }
+        if (b > 0) flush(t, b - 1, pl, ph);
+        else if (t > 0) flush(t - 1, RB - 1, pl, ph);
+        pl = al;
+        ph = ah;
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
     }
-    flush(TB - 1, pl, ph);
+    flush(TB - 1, RB - 1, pl, ph);
 
     // Q4_K min term, once per group of four super-blocks (or at the end);
     // lanes whose super-block lies past the end contribute zero
@@ -412,9 +436,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
         const int gbase = (it & 4);  // ring slots of this group: gbase .. gbase + 3
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-          const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * 16;
+          const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * AMS;
           const v8h ahv = *(const v8h*)src;
-          const v8h alv = *(const v8h*)(src + 8);
+          const v8h alv = *(const v8h*)(src + AMLO);
 #pragma unroll
           for (int b = 0; b < RB; ++b) {
             yacc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi[b], ahv, yacc[b][t], 0, 0, 0);
@@ -424,27 +448,49 @@ __global__ __launch_bounds__(64 * NW, 1) void k_qgemm(GemmParams p) {
         }
       }
     }
-    act_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
+    items_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
     __syncthreads();
   };
 
-  // ---- prologue: weights for the first two super-blocks, first stage
-  uint32_t rawA[RB][RAW], rawB[RB][RAW];
+  // ---- prologue: the first weights and activation stage are requested
+  // first, so that their latency overlaps the pre-scale scan below.
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, rawA[b]);
-    load_raw<QT>(wr, wrow_off[b] + (uint32_t)((s0 + 1) * BYTES), g4, rawB[b]);
+  for (int b = 0; b < RB; ++b) load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, raw[b]);
+  act_dma(0, s0);
+  items_load(s0);
+
+  // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
+  // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
+  if (tid < TOK) {
+    float esc = 1.0f;
+    if constexpr (MINS) {
+      // sixteen independent loads in flight per round
+      float mx = 0.0f;
+      const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
+      for (int64_t sb = s0; sb < s1; sb += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
+#pragma unroll
+        for (int u = 0; u < 16; ++u) mx = (sb + u < s1) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
+      }
+      if (mx > 0.0f) {
+        int e = 0;
+        (void)frexpf(mx, &e);
+        e = e < -100 ? -100 : (e > 100 ? 100 : e);
+        esc = ldexpf(1.0f, -e);
+      }
+    }
+    s_esc[tid] = esc;
   }
-  act_load(s0);
-  act_store(0, 0);
+  if constexpr (MINS) {
+    for (int i = tid; i < 2 * AMLO; i += NTH) s_amin[i] = (_Float16)0.0f;
+  }
+  __syncthreads();
+  items_store(0, 0);
   __syncthreads();
 
-  int64_t sb = s0;
-  for (; sb + 1 < s1; sb += 2) {
-    step(sb, rawA);
-    step(sb + 1, rawB);
-  }
-  if (sb < s1) step(sb, rawA);
+  for (int64_t sb = s0; sb < s1; ++sb) step(sb);
 
   // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
@@ -587,18 +633,29 @@ static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s
   }
 }
 
-// Tile configurations: cfg 0 = 4 waves x 2 row blocks (128 rows, one wave per
-// SIMD), cfg 1 = 4 waves x 1 row block (64 rows), cfg 2 = 8 waves x 1 row
-// block (128 rows, two waves per SIMD).  The LM head (argmax) uses cfg 1.
+// Tile configurations (waves x row blocks of 16 rows, tokens):
+//   cfg 1: 4 x 1 (64 rows), up to 160 tokens
+//   cfg 2: 8 x 1 (128 rows), up to 160 tokens
+//   cfg 3: 8 x 2 (256 rows), up to 80 tokens
+//   cfg 4: 4 x 2 (128 rows), up to 80 tokens, two work-groups per CU
+// The LM head (argmax) uses cfg 1.
 template <int QT>
 static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (argmax) return launch_q<QT, 4, 1, true>(p, tb, grid, s);
-  if (cfg == 0) return launch_q<QT, 4, 2, false>(p, tb, grid, s);
   if (cfg == 1) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
-  return launch_q<QT, 8, 1, false>(p, tb, grid, s);
+  if (cfg == 2) return launch_q<QT, 8, 1, false>(p, tb, grid, s);
+  const bool c3 = (cfg == 3);
+  switch (tb) {
+    case 1: return c3 ? launch_k<QT, 1, 8, 2, false>(p, grid, s) : launch_k<QT, 1, 4, 2, false>(p, grid, s);
+    case 2: return c3 ? launch_k<QT, 2, 8, 2, false>(p, grid, s) : launch_k<QT, 2, 4, 2, false>(p, grid, s);
+    case 3: return c3 ? launch_k<QT, 3, 8, 2, false>(p, grid, s) : launch_k<QT, 3, 4, 2, false>(p, grid, s);
+    case 4: return c3 ? launch_k<QT, 4, 8, 2, false>(p, grid, s) : launch_k<QT, 4, 4, 2, false>(p, grid, s);
+    default: return c3 ? launch_k<QT, 5, 8, 2, false>(p, grid, s) : launch_k<QT, 5, 4, 2, false>(p, grid, s);
+  }
 }
 
-int qgemm_cfg_rows(int cfg) { return cfg == 1 ? 64 : 128; }
+int qgemm_cfg_rows(int cfg) { return cfg == 1 ? 64 : (cfg == 3 ? 256 : 128); }
+int qgemm_cfg_max_tb(int cfg) { return cfg >= 3 ? 5 : 10; }
 
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);

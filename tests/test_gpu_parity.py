@@ -140,26 +140,25 @@ def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
     ws = None
     if split:
-        nb = max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16)
-        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
     assert_close_rows(y, ref, f"qgemm {qtype} {M}x{N}x{K} split={split}")
 
 
 @pytest.mark.parametrize("qtype", [12, 14])
-@pytest.mark.parametrize("tile", ["0", "1", "2"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K", [(148, 333, 2048), (37, 130, 1024), (160, 256, 512)])
 def test_qgemm_every_tile_configuration(dl, monkeypatch, qtype, tile, M, N, K):
-    """Each work-group shape (128 rows as 4 waves x 32 or 8 waves x 16, and
-    64 rows as 4 waves x 16), pinned through DLLM_QGEMM_TILE, on ragged rows
-    and tokens, split and unsplit."""
+    """Each work-group shape (64 rows as 4 waves x 16, 128 rows as 8 waves x
+    16, and over at most 80 tokens 256 rows as 8 waves x 32 or 128 rows as 4
+    waves x 32), pinned through DLLM_QGEMM_TILE, on ragged rows and tokens,
+    split and unsplit."""
     monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
     _say(f"qgemm tile={tile} qtype={qtype} M={M} N={N} K={K}")
     w = _weights(qtype, N, K, 11, f"t-{N}-{K}")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 11, f"tx-{M}-{K}").numpy())
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
-    nb = max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16)
-    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     xd = torch.from_numpy(xq).to(DEV)
     wd = w.to(DEV)
     for workspace in (ws, None):
@@ -177,7 +176,7 @@ def test_qgemm_full_size_layers(dl, qtype, N, K):
     w = _weights(qtype, N, K, 42, f"layer-{qtype}-{N}-{K}")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 42, f"act-{K}").numpy())
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
-    ws = torch.empty(max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
     assert_close_rows(y, ref, f"full qgemm {qtype} {N}x{K}")
 
@@ -188,7 +187,7 @@ def test_qgemm_gate_up_shape_sampled(dl):
     qtype, N, K, M = 12, 24576, 4096, 148
     w = _weights(qtype, N, K, 42, "gateup")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 42, "gateup-x").numpy())
-    ws = torch.empty(max(dl.qgemm_workspace_bytes(qtype, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
     toks = [0, 57, 146, 147]
     ref_rows = oracle.gemm(qtype, w.numpy(), N, K, xq[toks], len(toks))
@@ -263,11 +262,31 @@ def test_qgemm_deterministic(dl):
     N, K, M = 4096, 4096, 148
     w = _weights(12, N, K, 9, "det").to(DEV)
     xq = dl.quantize_q8k(synth.normal_f32((M, K), 9, "detx").to(DEV))
-    ws = torch.empty(max(dl.qgemm_workspace_bytes(12, N, K, M), 16), dtype=torch.uint8, device=DEV)
+    ws = dl.qgemm_workspace(12, N, K, M, DEV)
     a = dl.qgemm(12, w, N, K, xq, M, workspace=ws).clone()
     b = dl.qgemm(12, w, N, K, xq, M, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_qgemm_shared_workspace_across_shapes(dl):
+    """One workspace, sized for the largest, serves K-split calls of
+    different shapes in stream order (whole oracle rows of four tokens)."""
+    M = 148
+    shapes = [(12, 4096, 4096), (12, 12288, 4096), (14, 4096, 12288), (12, 4096, 4096), (14, 2048, 3072)]
+    nb = max(dl.qgemm_workspace_bytes(q, N, K, M) for q, N, K in shapes)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    toks = [0, 31, 100, 147]
+    xs = {}
+    for i, (q, N, K) in enumerate(shapes):
+        _say(f"shared workspace call {i}: qtype={q} N={N} K={K}")
+        assert dl.qgemm_workspace_bytes(q, N, K, M) > 0  # every shape here splits K
+        w = _weights(q, N, K, 13, f"ws-{q}-{N}-{K}")
+        if K not in xs:
+            xs[K] = oracle.quantize_q8k(synth.normal_f32((M, K), 13, f"wsx-{K}").numpy())
+        y = dl.qgemm(q, w.to(DEV), N, K, torch.from_numpy(xs[K]).to(DEV), M, workspace=ws).cpu().numpy()
+        ref = oracle.gemm(q, w.numpy(), N, K, xs[K][toks], len(toks))
+        assert_close_rows(y[toks], ref, f"shared workspace call {i}")
 
 
 # ------------------------------------------------------------- LM head ----
