@@ -44,7 +44,39 @@ def parse():
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--profile-dominant", action="store_true",
+                    help="for hardware-counter runs: a 256 MiB device copy (the counters' calibration), then "
+                         "--steps launches of the step's dominant GEMM (one layer's gate/up), then exit")
     return ap.parse_args()
+
+
+DOMINANT = ("qgemm_q4k", 2 * FFN, D)  # gate/up: the call that takes most of the step
+
+
+def profile_dominant(args):
+    """A known-size copy kernel (FETCH_SIZE / WRITE_SIZE of it calibrate the
+    counters), then the dominant GEMM call alone, as in the step."""
+    import torch
+    import diffusion_lm_gemm_amd as dl
+    import synth
+    dev = torch.device("cuda:0")
+    a = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    _, N, K = DOMINANT
+    L = args.L
+    w = synth.q4k_rows(N, K, args.seed, "L01.ffn_gate_up", dev)
+    xq = dl.quantize_q8k(synth.normal_f32((L, K), args.seed, "L01.h_norm", dev))
+    y = torch.empty((L, N), dtype=torch.float32, device=dev)
+    ws = dl.qgemm_workspace(dl.Q4_K, N, K, L, dev)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dl.qgemm(dl.Q4_K, w, N, K, xq, L, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"[profile-dominant] copy of {a.numel() * 4} bytes, then {args.steps} x qgemm Q4_K N={N} K={K} M={L}",
+          flush=True)
 
 
 def main():
@@ -55,6 +87,10 @@ def main():
             print("bench.py runs on one GPU only: this build has no multi-GPU path "
                   f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_dominant:
+        profile_dominant(args)
+        return
 
     import torch
     import diffusion_lm_gemm_amd as dl
@@ -113,12 +149,14 @@ def main():
 
     def add_quant(x, out):
         M, K = x.shape
-        calls.append(("quantize_q8k", lambda: dl.quantize_q8k(x, out), M * K * 4 + M * K // 256 * 292, 0))
+        calls.append(("quantize_q8k", lambda: dl.quantize_q8k(x, out), M * K * 4 + M * K // 256 * 292, 0,
+                      ("quantize_q8k", M, K)))
 
     def add_gemm(q, w, N, K, xq, y):
         byts = N * K // 256 * bb(q) + L * K // 256 * 292 + L * N * 4
         kind = "qgemm_q4k" if q == Q4 else "qgemm_q6k"
-        calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws), byts, 2 * L * N * K))
+        calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws), byts, 2 * L * N * K,
+                      (kind, N, K)))
 
     for lw in layers:
         add_quant(lw["x_norm"], xq_d)
@@ -136,7 +174,7 @@ def main():
     lm_bytes = (MASKED * D * 4 + MASKED * D // 256 * 292 + VOCAB * D // 256 * bb(Q6)
                 + MASKED * VOCAB * 4 + MASKED * 4)
     calls.append(("lmhead_q6k", lambda: dl.lmhead_masked(Q6, w_out, VOCAB, D, hidden, rows, logits, amax, ws_lm),
-                  lm_bytes, 2 * MASKED * VOCAB * D))
+                  lm_bytes, 2 * MASKED * VOCAB * D, ("lmhead_q6k", VOCAB, D)))
     step_bytes = sum(c[2] for c in calls)
     step_ops = sum(c[3] for c in calls)
 
@@ -172,6 +210,8 @@ def main():
           f"(wall {1e3 * wall / args.steps:.4f} ms/step)", file=sys.stderr, flush=True)
 
     # ---------------- per-call durations (eager, HIP events on the launch stream)
+    # Every call is bracketed by events on the stream it is launched on; calls
+    # are grouped by kind and by shape.
     reps = 3
     per = {}
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
@@ -182,27 +222,35 @@ def main():
             b.record()
         torch.cuda.synchronize()
         for (a, b), c in zip(evs, calls):
-            k = per.setdefault(c[0], [0.0, 0, 0, 0])
-            k[0] += a.elapsed_time(b)
-            k[1] += 1
-            k[2] += c[2]
-            k[3] += c[3]
-    kinds = {}
-    for k, (ms, n, byts, ops) in per.items():
-        kinds[k] = {"launches_per_step": n // reps, "avg_ms": ms / n,
-                    "GBps": byts / (ms * 1e-3) / 1e9, "TOPS": ops / (ms * 1e-3) / 1e12 if ops else 0.0,
-                    "share_of_eager_time": 0.0}
-    tot = sum(v[0] for v in per.values())
-    for k in kinds:
-        kinds[k]["share_of_eager_time"] = per[k][0] / tot
-    dom = max(per, key=lambda k: per[k][0])
+            for key in (c[0], c[4]):
+                k = per.setdefault(key, [0.0, 0, 0, 0])
+                k[0] += a.elapsed_time(b)
+                k[1] += 1
+                k[2] += c[2]
+                k[3] += c[3]
+
+    def stats(key):
+        ms, n, byts, ops = per[key]
+        return {"launches_per_step": n // reps, "avg_ms": ms / n, "GBps": byts / (ms * 1e-3) / 1e9,
+                "TOPS": ops / (ms * 1e-3) / 1e12 if ops else 0.0}
+    kind_keys = [k for k in per if isinstance(k, str)]
+    shape_keys = [k for k in per if isinstance(k, tuple)]
+    tot = sum(per[k][0] for k in kind_keys)
+    kinds = {k: dict(stats(k), share_of_eager_time=per[k][0] / tot) for k in kind_keys}
+    shapes = {f"{k[0]} {k[1]}x{k[2]}": dict(stats(k), share_of_eager_time=per[k][0] / tot) for k in shape_keys}
+    dom = max(shape_keys, key=lambda k: per[k][0])
     dms, dn, dbytes, dops = per[dom]
+    dom_name = f"{dom[0]}_{dom[1]}x{dom[2]}"
     achieved = dbytes / (dms * 1e-3) / 1e9
     print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
+    print(f"[bench] per-call shapes: " + json.dumps(shapes), file=sys.stderr, flush=True)
 
     # ---------------- HBM traffic from committed counter summaries ---------
+    # FETCH_SIZE + WRITE_SIZE of the dominant call's kernel, scaled by the
+    # same counters on a copy of known size; valid only for the kernel
+    # sources it was measured on.
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_step_L{L}.txt")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom_name}_L{L}.txt")
     if os.path.exists(tpath):
         kv = dict(l.split("=", 1) for l in open(tpath).read().split() if "=" in l)
         src_hash = _kernel_hash()
@@ -239,7 +287,7 @@ def main():
         "step_frac_mfma": round(step_ops / step_s / 1e12 / INT8_PEAK_TOPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "step_int8_ops": step_ops,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_call_ms": round(dms / dn, 5), "calls_per_step": dn // reps,
                      "algorithmic_bytes_per_call": dbytes // dn,
@@ -247,6 +295,8 @@ def main():
                      "frac_mfma": round(dops / (dms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)},
         "per_call_kind": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                           for k, v in kinds.items()},
+        "per_call_shape": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                           for k, v in shapes.items()},
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),
     }
@@ -256,7 +306,7 @@ def main():
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "qgemm.hip", "quantize.hip"):
+    for f in ("common.hpp", "qgemm.hip", "quantize.hip", "abi.hip"):
         h.update(open(os.path.join(ROOT, "diffusion_lm_gemm_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
