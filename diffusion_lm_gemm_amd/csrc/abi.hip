@@ -108,8 +108,8 @@ struct Plan {
 // Time of one super-block step of a work-group with a full token tile, per
 // tile configuration, in microseconds, and its factor for Q6_K (heavier
 // unpacking), fitted to measured single-GEMM times on MI355X at 148 tokens.
-constexpr double kCfgStepUs[5] = {0.0, 2.709, 2.736, 2.785, 1.739};
-constexpr double kCfgQ6Factor[5] = {0.0, 1.060, 1.379, 1.735, 1.819};
+constexpr double kCfgStepUs[5] = {0.0, 2.528, 2.636, 2.690, 1.658};
+constexpr double kCfgQ6Factor[5] = {0.0, 1.025, 1.185, 1.738, 1.708};
 
 // DLLM_QGEMM_TILE=1|2|3|4 pins the tile configuration (for testing every
 // configuration on any shape); unset, the planner chooses.

@@ -226,7 +226,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // read while the next is written.  A lane's 16-byte read of one token's
   // eight values has consecutive tokens at consecutive 16-byte slots, so the
   // reads of a wave hit distinct banks.
-  __shared__ __attribute__((aligned(16))) uint8_t s_act[2][TOKP * ACT_ROW];
+  // The two stages are separate objects.  Where each step names them directly
+  // the compiler sees that the buffer-to-LDS loads filling one stage do not
+  // alias the reads of the other, and does not wait for those loads before
+  // the reads.
+  __shared__ __attribute__((aligned(16))) uint8_t s_act0[TOKP * ACT_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t s_act1[TOKP * ACT_ROW];
   constexpr int AMS = 8;               // halves per token record of the ring
   constexpr int AMLO = 8 * TOK * AMS;  // offset of the low halves
   // d_x staging: items (a token, or for Q4_K a (token, half q) pair that
@@ -270,14 +275,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // and so is every store (to its own LDS address).
   const uint32_t dma_tok0 = (uint32_t)((m0 + wv * DPW * 4 + (lane >> 4)) * SB * Q8K_BYTES) + 4;
   const uint32_t tok_step = (uint32_t)(4 * SB * Q8K_BYTES);
-  auto act_dma = [&](int buf, int64_t sb) {
+  auto act_dma = [&](uint8_t* stage, int64_t sb) {
     const uint32_t soff = (uint32_t)(sb * Q8K_BYTES);
 #pragma unroll
     for (int k = 0; k < DPW; ++k) {
       const int tok = (wv * DPW + k) * 4 + (lane >> 4);
       const uint32_t voff = dma_tok0 + k * tok_step + 16 * ((lane & 15) ^ (tok & 15));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(s_act[buf] + (wv * DPW + k) * 1024), 16, voff, soff, 0, 0);
+          xr, (__attribute__((address_space(3))) void*)(stage + (wv * DPW + k) * 1024), 16, voff, soff, 0, 0);
     }
   };
   // idx_b: Q4_K bsum pairs (2j, 2j+1) for j = 4q .. 4q+3, one per dword
@@ -344,11 +349,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // the end of a group of four, publish the next stage's d_x.  The barrier at
   // the end also waits for every load in flight.
   uint32_t raw[RB][RAW];
-  auto step = [&](int64_t sb) {
+  // act: this step's stage; act_next: the other one, filled for sb + 1;
+  // buf == (sb - s0) & 1 indexes the d_x stages.
+  auto step = [&](int64_t sb, const uint8_t* act, uint8_t* act_next, int buf) {
     const int it = (int)(sb - s0);
-    const int buf = it & 1, slot = it & 3;
+    const int slot = it & 3;
     const bool more = sb + 1 < s1;
-    act_dma(buf ^ 1, sb + 1);  // past the end: an unread stage
+    act_dma(act_next, sb + 1);  // past the end: an unread stage
     items_load(sb + 1);
     v4i alo[RB][4], ahi[RB][4];
     float dsel[RB][4];
@@ -372,7 +379,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
     // software-pipelined: the B fragments of token block t+1 are read while
     // block t's MFMAs run, and each (token block, row block) tile's integer
     // sums are folded into y while the next tile's MFMAs run.
-    const uint8_t* act = s_act[buf];
     int bunit[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) bunit[c] = 16 * (act_unit<QT>(c, g4) ^ r);  // token t*16 + r has (tok & 15) == r
@@ -456,7 +462,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // first, so that their latency overlaps the pre-scale scan below.
 #pragma unroll
   for (int b = 0; b < RB; ++b) load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, raw[b]);
-  act_dma(0, s0);
+  act_dma(s_act0, s0);
   items_load(s0);
 
   // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
@@ -490,7 +496,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   items_store(0, 0);
   __syncthreads();
 
-  for (int64_t sb = s0; sb < s1; ++sb) step(sb);
+  if constexpr (RB == 1) {
+    // two steps per iteration, each naming its stages directly
+    int64_t sb = s0;
+    for (; sb + 1 < s1; sb += 2) {
+      step(sb, s_act0, s_act1, 0);
+      step(sb + 1, s_act1, s_act0, 1);
+    }
+    if (sb < s1) step(sb, s_act0, s_act1, 0);
+  } else {
+    // one step per iteration (fewer live registers; the compiler then waits
+    // for the stage loads before the step's first LDS read)
+    for (int64_t sb = s0; sb < s1; ++sb) {
+      const int buf = (int)(sb - s0) & 1;
+      step(sb, buf ? s_act1 : s_act0, buf ? s_act0 : s_act1, buf);
+    }
+  }
 
   // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;

