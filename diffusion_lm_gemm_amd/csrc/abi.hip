@@ -143,6 +143,8 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
       const int64_t sps = cdiv(SB, S);
       const int64_t s_eff = cdiv(SB, sps);
       if (s_eff != S) continue;
+      // the reduction reads the partials through 32-bit buffer offsets
+      if (S > 1 && (S + 3) * M * N * 4 >= ((int64_t)1 << 32)) break;
       const int64_t wgs = n_tiles * m_tiles * S;
       const int64_t rounds = cdiv(wgs, kCUs);
       double cost = (double)rounds * (double)sps * step_us;
@@ -243,9 +245,19 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
 
 static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
+// Key slots per gathered row: one per 64-row tile (tiled path) or one per
+// wave (streaming path), whichever is more.
 int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_rows) {
   if (check_qtype(qtype) || N <= 0 || K <= 0 || K % 256 || n_rows <= 0) return -1;
-  return align256(n_rows * (K / 256) * Q8K_BYTES) + cdiv(N, 64) * n_rows * 8;
+  const int64_t slots = cdiv(N, 64) > lmhead_stream_waves() ? cdiv(N, 64) : lmhead_stream_waves();
+  return align256(n_rows * (K / 256) * Q8K_BYTES) + slots * n_rows * 8;
+}
+
+// DLLM_LMHEAD_TILED=1 selects the tiled GEMM path even where the streaming
+// kernel applies (for testing both).
+static bool lmhead_force_tiled() {
+  const char* e = getenv("DLLM_LMHEAD_TILED");
+  return e && e[0] == '1' && !e[1];
 }
 
 int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
@@ -280,6 +292,20 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   uint64_t* keys = (uint64_t*)((uint8_t*)workspace + align256(n_rows * SB * Q8K_BYTES));
   if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, s), "dllm_lmhead_masked gather/quantize launch")))
     return rc;
+  if (lmhead_stream_fits(K, n_rows) && !lmhead_force_tiled()) {
+    LmParams lp;
+    lp.w = (const uint8_t*)w;
+    lp.xq = xq;
+    lp.logits = logits;
+    lp.keys = keys;
+    lp.N = N;
+    lp.SB = SB;
+    lp.M = n_rows;
+    lp.ldl = ldl;
+    if ((rc = hip_status(launch_lmhead_stream(qtype, lp, s), "dllm_lmhead_masked stream launch"))) return rc;
+    return hip_status(launch_argmax_finalize(keys, lmhead_stream_slots(N), n_rows, argmax, s),
+                      "dllm_lmhead_masked argmax launch");
+  }
   GemmParams p;
   p.w = (const uint8_t*)w;
   p.xq = xq;

@@ -17,6 +17,17 @@ struct GemmParams {
   int sps;               // super-blocks per split
 };
 
+// Streaming LM head: at most 32 gathered Q8_K rows (xq, [M][SB] records)
+// against all N weight rows; keys[wave * M + m] get each wave's best key.
+struct LmParams {
+  const uint8_t* w;
+  const uint8_t* xq;
+  float* logits;
+  uint64_t* keys;
+  int64_t N, SB, M;
+  int64_t ldl;
+};
+
 hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
                                hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
@@ -27,6 +38,10 @@ int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s);
+bool lmhead_stream_fits(int64_t K, int64_t n_rows);
+int lmhead_stream_waves();             // the most waves (key slots per row) it uses
+int64_t lmhead_stream_slots(int64_t N);  // the waves it uses for N rows
+hipError_t launch_lmhead_stream(int qtype, const LmParams& p, hipStream_t s);
 hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s);
 hipError_t launch_partials(int qtype, const uint8_t* w, int64_t N, int64_t SB, const uint8_t* xq, int64_t M,
                            int32_t* P, hipStream_t s);

@@ -31,175 +31,9 @@
 // second kernel sums them in split order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "unpack.hpp"
 
 namespace dllm {
-
-// LDS holds each token's 256 activation bytes in natural K order as sixteen
-// 16-byte units, unit u of token tok stored at unit slot u ^ (tok & 15): the
-// 16-byte B-fragment reads of 16 consecutive tokens then fall in 16 distinct
-// slots (no bank conflicts), and the rows stay dense, so buffer-to-LDS loads
-// (which write 16 bytes per lane to consecutive addresses) can fill them by
-// choosing which global unit each lane fetches.
-constexpr int ACT_ROW = 256;
-
-template <int QT>
-struct QTr;
-template <>
-struct QTr<QT_Q4K> {
-  static constexpr int BYTES = Q4K_BYTES;
-  static constexpr int SHIFT = 3;
-  static constexpr int RAW = 12;  // dwords of raw block data per lane
-};
-template <>
-struct QTr<QT_Q6K> {
-  static constexpr int BYTES = Q6K_BYTES;
-  static constexpr int SHIFT = 7;
-  static constexpr int RAW = 26;
-};
-
-__device__ __forceinline__ uint32_t pkmul(uint32_t a, uint32_t b) {
-  return as_u32(as_u16x2(a) * as_u16x2(b));
-}
-
-// K order of the MFMA fragments.  For K chunk c (0..3) of a super-block,
-// lane group g4 (lanes 16 g4 .. 16 g4 + 15) holds 16 consecutive K values,
-// activation unit act_unit<QT>(c, g4) (bytes 16 u .. 16 u + 15 of the block).
-// Chunks are chosen so that each lane unpacks them from bytes it loads itself,
-// with a nibble choice that is the same for every lane of a chunk:
-//   Q4_K: chunk c = (half h = c >> 1, nibble n = c & 1): the n-nibbles of
-//         quant bytes 64 h + 16 g4 .. + 15, i.e. sub-block 4h + 2(g4 >> 1) + n,
-//         positions 16 (g4 & 1) .. + 15.
-//   Q6_K: chunk c = (half h = c >> 1, nibble n = c & 1): low-bit bytes
-//         64 h + 16 g4 .. + 15 (nibble n) with high-bit bytes
-//         32 h + 16 (g4 & 1) .. + 15, i.e. quarter k = 2n + (g4 >> 1) of half h,
-//         positions 16 (g4 & 1) .. + 15.
-template <int QT>
-__device__ __forceinline__ int act_unit(int c, int g4) {
-  if constexpr (QT == QT_Q4K) return 8 * (c >> 1) + 4 * (g4 >> 1) + 2 * (c & 1) + (g4 & 1);
-  else return 8 * (c >> 1) + 4 * (c & 1) + g4;
-}
-
-// Five dwords at the dword-aligned byte offset a (16 bytes starting at a or
-// a + 2, see unpack).
-__device__ __forceinline__ void ld5(rsrc_t r, uint32_t a, uint32_t* d) {
-  const v4u v = buf_ld128(r, a);
-  d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-  d[4] = buf_ld32(r, a + 16);
-}
-
-// Raw (packed) bytes of the lane's part of one weight super-block at byte
-// offset `off` of the weight buffer.  Reads past the end of the buffer (rows
-// beyond N) return zeros, so padded rows contribute nothing.
-template <int QT>
-__device__ __forceinline__ void load_raw(rsrc_t wr, uint32_t off, int g4, uint32_t (&raw)[QTr<QT>::RAW]) {
-  if constexpr (QT == QT_Q4K) {
-    // header (d | dmin, 12 scale/min bytes), then quant bytes 16 g4 .. and
-    // 64 + 16 g4 .. of the 128-byte quant area.  Blocks are 144 bytes, so
-    // every piece is 16-byte aligned.
-    const v4u hdr = buf_ld128(wr, off);
-    const v4u q0 = buf_ld128(wr, off + 16 + 16 * g4);
-    const v4u q1 = buf_ld128(wr, off + 16 + 64 + 16 * g4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      raw[i] = hdr[i];
-      raw[4 + i] = q0[i];
-      raw[8 + i] = q1[i];
-    }
-  } else {
-    // Blocks are 210 bytes, so a block starts at a dword boundary or two
-    // bytes past one; each 16-byte field is fetched as the five dwords that
-    // cover it and aligned when unpacked.  Fields: low-bit bytes 64h + 16 g4
-    // (h = 0, 1), high-bit bytes 128 + 32h + 16 (g4 & 1), the 16 scales at
-    // 192, and the f16 d at 208 (a 16-bit load: a dword there would reach
-    // past the end of the buffer for a dword-aligned last block, and the
-    // buffer's range check would zero all of it).
-    const uint32_t a = off & ~3u;
-    ld5(wr, a + 16 * g4, raw);
-    ld5(wr, a + 64 + 16 * g4, raw + 5);
-    ld5(wr, a + 128 + 16 * (g4 & 1), raw + 10);
-    ld5(wr, a + 160 + 16 * (g4 & 1), raw + 15);
-    ld5(wr, a + 192, raw + 20);
-    raw[25] = buf_ld16(wr, off + 208);
-  }
-}
-
-// Q6_K: four quants (bytes, 0..63) with one signed scale s -> the two int8
-// planes of s*(q-32).  In 16-bit lanes 2s*q - 64s = 2 s (q-32) = 256 hi + 2 lo,
-// so the high byte is hi and the low byte is 2 lo.
-__device__ __forceinline__ void q6_planes(uint32_t q, uint32_t s2, uint32_t c64, uint32_t& lo, uint32_t& hi) {
-  const uint32_t e = __builtin_amdgcn_perm(0u, q, 0x0c020c00u);  // q0, q2 in u16 lanes
-  const uint32_t o = __builtin_amdgcn_perm(0u, q, 0x0c030c01u);  // q1, q3
-  const uint32_t we = as_u32(as_u16x2(e) * as_u16x2(s2) + as_u16x2(c64));
-  const uint32_t wo = as_u32(as_u16x2(o) * as_u16x2(s2) + as_u16x2(c64));
-  hi = __builtin_amdgcn_perm(wo, we, 0x07030501u);
-  lo = __builtin_amdgcn_perm(wo, we, 0x06020400u) >> 1;
-}
-
-// Unpack raw bytes into the two int8 planes of the four 16x64 A fragments
-// (K order of act_unit) and return the super-block factor d.  soff: the byte
-// offset of the block mod 4 (Q6_K only: 0 or 2).
-template <int QT>
-__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, uint32_t soff, v4i (&alo)[4],
-                                        v4i (&ahi)[4]) {
-  if constexpr (QT == QT_Q4K) {
-    uint32_t sc03, sc47, mn03, mn47;
-    q4k_scales(raw[1], raw[2], raw[3], sc03, sc47, mn03, mn47);
-    const int jb0 = 2 * (g4 >> 1);  // sub-block byte of chunk (h, 0); chunk (h, 1) is the next one
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int h = c >> 1, n = c & 1;
-      const uint32_t scv = h ? sc47 : sc03;
-      const uint32_t sl = splat_byte_u16x2(scv & 0x07070707u, jb0 + n);
-      const uint32_t sh = splat_byte_u16x2((scv >> 3) & 0x07070707u, jb0 + n);
-      uint32_t lo[4], hi[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t v = raw[4 + 4 * h + d];
-        const uint32_t nib = n ? q4k_hi_nibbles(v) : q4k_lo_nibbles(v);
-        lo[d] = pkmul(nib, sl);
-        hi[d] = pkmul(nib, sh);
-      }
-      alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
-      ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    return f16_bits_to_f32(raw[0]);
-  } else {
-    uint32_t ql[2][4], qh[2][4], sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ql[0][i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], soff);
-      ql[1][i] = __builtin_amdgcn_alignbyte(raw[5 + i + 1], raw[5 + i], soff);
-      qh[0][i] = __builtin_amdgcn_alignbyte(raw[10 + i + 1], raw[10 + i], soff);
-      qh[1][i] = __builtin_amdgcn_alignbyte(raw[15 + i + 1], raw[15 + i], soff);
-      sc[i] = __builtin_amdgcn_alignbyte(raw[20 + i + 1], raw[20 + i], soff);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int h = c >> 1, n = c & 1;
-      // scale index 8h + 4n + g4: byte g4 of scale dword 2h + n
-      const int s = (int)(int8_t)(sc[2 * h + n] >> (8 * g4));
-      const uint32_t s2 = ((uint32_t)(2 * s) & 0xFFFFu) * 0x10001u;
-      const uint32_t c64 = ((uint32_t)(-64 * s) & 0xFFFFu) * 0x10001u;
-      const int hsh = 2 * (2 * n + (g4 >> 1));  // high bits of quarter k = 2n + (g4 >> 1)
-      uint32_t lo[4], hi[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo4 = n ? q4k_hi_nibbles(ql[h][d]) : q4k_lo_nibbles(ql[h][d]);
-        const uint32_t hi2 = (qh[h][d] >> hsh) & 0x03030303u;
-        q6_planes(lo4 | (hi2 << 4), s2, c64, lo[d], hi[d]);
-      }
-      alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
-      ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    return f16_bits_to_f32(raw[25]);
-  }
-}
-
-__device__ __forceinline__ uint32_t f32_order_bits(float v) {
-  if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // NW waves per work-group, RB row blocks of 16 weight rows per wave: the tile
 // is 16 * RB * NW rows x 16 * TB tokens.  Each B fragment read from LDS feeds
@@ -569,15 +403,39 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   }
 }
 
-// Sum of the K-split partial tiles in split order (deterministic).
+// Sum of the K-split partial tiles in split order (deterministic): each
+// thread owns four consecutive elements of the M x N partial tile and keeps
+// four slices' loads in flight.  The slices are read through a buffer
+// resource, so slices past S (and elements past M x N) read as zero.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int S, int64_t M,
                                                     int64_t N, float* __restrict__ y, int64_t ldy) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * N) return;
-  const int64_t m = i / N, n = i - m * N;
-  float acc = ws[i];
-  for (int s = 1; s < S; ++s) acc += ws[(int64_t)s * M * N + i];
-  y[m * ldy + n] = acc;
+  const int64_t MN = M * N;
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= MN) return;
+  const rsrc_t r = make_rsrc(ws, (int64_t)S * MN * 4);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (e0 + 4 <= MN) {
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      v4u v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)(s0 + u) * MN + e0) * 4));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += __builtin_bit_cast(v4f, v[u]);
+    }
+  } else {
+    // the last, partial group of four: element loads (a 16-byte load that
+    // reaches past the end of the range would read as zero whole)
+    for (int s0 = 0; s0 < S; ++s0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] += __builtin_bit_cast(float, buf_ld32(r, (uint32_t)(((int64_t)s0 * MN + e0 + i) * 4)));
+  }
+  int64_t m = e0 / N, n = e0 - m * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e0 + i < MN) y[m * ldy + n] = acc[i];
+    if (++n == N) { n = 0; ++m; }
+  }
 }
 
 // argmax[m] = lowest row index of the largest logit, from per-tile keys.
@@ -685,7 +543,7 @@ hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 gr
 
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
   const int64_t total = M * N;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, ws, S, M, N, y, ldy);
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, ws, S, M, N, y, ldy);
   return hipGetLastError();
 }
 

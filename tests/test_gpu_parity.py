@@ -307,16 +307,25 @@ def _check_argmax(logits_gpu, am_gpu, ref_logits, ref_am, what):
     _say(f"{what}: argmax identical in {ref_logits.shape[0] - exceptions}/{ref_logits.shape[0]} rows")
 
 
+@pytest.mark.parametrize("qtype", [12, 14])
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 7, 32, 40])
-def test_lmhead_small(dl, n_rows):
-    N, K, M = 1000, 512, 148
-    w = _weights(14, N, K, 13, "lm-small")
+def test_lmhead_small(dl, monkeypatch, qtype, tiled, n_rows):
+    """Both LM-head paths: the streaming kernel (<= 32 rows, K <= 4096) and
+    the tiled GEMM (forced with DLLM_LMHEAD_TILED=1, and taken for 40 rows),
+    on a vocabulary that is not a multiple of any tile (1000 rows) and K of
+    three super-blocks."""
+    if tiled:
+        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
+    N, K, M = 1000, 768, 148
+    _say(f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows}")
+    w = _weights(qtype, N, K, 13, f"lm-small-{qtype}")
     h = synth.normal_f32((M, K), 13, "lm-h")
     rows = synth.distinct_rows(n_rows, M, 13, f"rows-{n_rows}")
-    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
-    logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    ref, ref_am = oracle.lmhead(qtype, w.numpy(), N, K, h.numpy(), rows.numpy())
+    logits, am = dl.lmhead_masked(qtype, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
     logits = logits.cpu().numpy(); am = am.cpu().numpy()
-    assert_close_rows(logits, ref, f"lmhead n_rows={n_rows}")
+    assert_close_rows(logits, ref, f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows}")
     _check_argmax(logits, am, ref, ref_am, f"lmhead n_rows={n_rows}")
 
 
