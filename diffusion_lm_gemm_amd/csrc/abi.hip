@@ -108,14 +108,33 @@ struct Plan {
 // Time of one super-block step of a work-group with a full token tile, per
 // tile configuration, in microseconds, and its factor for Q6_K (heavier
 // unpacking), fitted to measured single-GEMM times on MI355X at 148 tokens.
-constexpr double kCfgStepUs[5] = {0.0, 2.528, 2.636, 2.690, 1.658};
-constexpr double kCfgQ6Factor[5] = {0.0, 1.025, 1.185, 1.738, 1.708};
+constexpr double kCfgStepUs[6] = {0.0, 2.610, 2.771, 2.748, 1.610, 1.871};
+constexpr double kCfgQ6Factor[6] = {0.0, 0.873, 1.173, 1.864, 2.002, 1.039};
 
-// DLLM_QGEMM_TILE=1|2|3|4 pins the tile configuration (for testing every
+// Measured best (tile configuration, K split) for the linear layers of the
+// LLaDA-8B step (d = 4096, FFN 12288; Q4_K, and Q6_K for attn_v / ffn_down)
+// at canvases of 129..160 tokens, from timing every candidate on MI355X.
+// Shapes not listed go to the cost model below.
+struct Tuned {
+  int qtype;
+  int64_t N, K, m_lo, m_hi;
+  int cfg, S;
+};
+constexpr Tuned kTuned[] = {
+    {12, 24576, 4096, 129, 160, 2, 1},  // gate + up
+    {12, 12288, 4096, 129, 160, 4, 1},  // Q + K + V
+    {12, 8192, 4096, 129, 160, 3, 4},   // Q + K (V in Q6_K)
+    {12, 4096, 4096, 129, 160, 4, 4},   // O
+    {14, 4096, 4096, 129, 160, 5, 4},   // V
+    {12, 4096, 12288, 129, 160, 3, 8},  // down
+    {14, 4096, 12288, 129, 160, 5, 8},  // down
+};
+
+// DLLM_QGEMM_TILE=1..5 pins the tile configuration (for testing every
 // configuration on any shape); unset, the planner chooses.
 static int forced_cfg() {
   const char* e = getenv("DLLM_QGEMM_TILE");
-  if (!e || e[0] < '1' || e[0] > '4' || e[1]) return -1;
+  if (!e || e[0] < '1' || e[0] > '5' || e[1]) return -1;
   return e[0] - '0';
 }
 
@@ -128,7 +147,18 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   double best_cost = 1e300;
   const int64_t SB = K / 256;
   const int fc = forced_cfg();
-  for (int cfg : {4, 3, 2, 1}) {
+  if (fc < 0) {
+    for (const Tuned& t : kTuned) {
+      if (t.qtype != qtype || t.N != N || t.K != K || M < t.m_lo || M > t.m_hi) continue;
+      const int S = allow_split ? t.S : 1;
+      const int64_t sps = cdiv(SB, S);
+      if (cdiv(SB, sps) != S) break;
+      const int max_tb = qgemm_cfg_max_tb(t.cfg);
+      const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
+      return Plan{tb, t.cfg, cdiv(N, qgemm_cfg_rows(t.cfg)), cdiv(M, 16 * tb), S, (int)sps};
+    }
+  }
+  for (int cfg : {5, 4, 3, 2, 1}) {
     if (fc >= 0 && cfg != fc) continue;
     const int64_t rows = qgemm_cfg_rows(cfg);
     const int64_t n_tiles = cdiv(N, rows);

@@ -33,7 +33,8 @@ hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows,
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
 // cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
 // 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up
-// to 80 tokens).  argmax forces cfg 1.
+// to 80 tokens; 5: 64 rows, 4 waves x 16, one activation stage, two
+// work-groups per CU).  argmax forces cfg 1.
 int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);

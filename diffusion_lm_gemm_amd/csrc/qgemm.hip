@@ -40,8 +40,13 @@ namespace dllm {
 // 2 * RB MFMAs.
 // Four-wave tiles of at most 80 tokens fit two work-groups per CU (two waves
 // per SIMD, each with its own barrier); larger tiles run one per CU.
-template <int QT, int TB, int NW, int RB, bool ARGMAX>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm(GemmParams p) {
+// ST = 2: the activation stage of the next super-block is loaded while this
+// one is used (double buffer, one barrier per step).  ST = 1: one stage,
+// loaded at the start of each step (two barriers per step); with 4 waves this
+// fits two work-groups per CU whose waits the other one's work fills.
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
+  constexpr bool ONE = (ST == 1);
   constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
   constexpr int NTH = 64 * NW;          // threads
   constexpr int ROWS = 16 * RB * NW;    // weight rows per work-group
@@ -65,9 +70,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // alias the reads of the other, and does not wait for those loads before
   // the reads.
   __shared__ __attribute__((aligned(16))) uint8_t s_act0[TOKP * ACT_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_act1[TOKP * ACT_ROW];
-  constexpr int AMS = 8;               // halves per token record of the ring
-  constexpr int AMLO = 8 * TOK * AMS;  // offset of the low halves
+  __shared__ __attribute__((aligned(16))) uint8_t s_act1[ONE ? 16 : TOKP * ACT_ROW];
+  constexpr int AMS = 8;                    // halves per token record of the ring
+  constexpr int RSLOTS = ONE ? 4 : 8;       // ring slots (one group, or two)
+  constexpr int AMLO = RSLOTS * TOK * AMS;  // offset of the low halves
   // d_x staging: items (a token, or for Q4_K a (token, half q) pair that
   // covers sub-blocks 4q .. 4q+3) are spread over all threads.  Token t's d_x
   // sits at slot t (written by its item with q = 0); every other item writes
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
   // unconditional and has its own address.
   constexpr int NITEM = MINS ? TOK * 2 : TOK;
   constexpr int IPT = (NITEM + NTH - 1) / NTH;  // items per thread
-  __shared__ float s_dx[2][TOK + IPT * NTH];
+  __shared__ float s_dx[ONE ? 1 : 2][TOK + IPT * NTH];
   __shared__ float s_esc[TOK];
   __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTH - NITEM) + 8 : 8];
   __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
@@ -189,8 +195,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
     const int it = (int)(sb - s0);
     const int slot = it & 3;
     const bool more = sb + 1 < s1;
-    act_dma(act_next, sb + 1);  // past the end: an unread stage
-    items_load(sb + 1);
+    if constexpr (ONE) {
+      act_dma(s_act0, sb);
+      items_load(sb);
+    } else {
+      act_dma(act_next, sb + 1);  // past the end: an unread stage
+      items_load(sb + 1);
+    }
     v4i alo[RB][4], ahi[RB][4];
     float dsel[RB][4];
 #pragma unroll
@@ -203,9 +214,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
         mh2[b] = mine ? raw[b][2] : mh2[b];
         mh3[b] = mine ? raw[b][3] : mh3[b];
       }
-      load_raw<QT>(wr, boff + BYTES, g4, raw[b]);
+      if constexpr (!ONE) load_raw<QT>(wr, boff + BYTES, g4, raw[b]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dsel[b][i] = __shfl(drow, 4 * g4 + i);
+    }
+    if constexpr (ONE) {
+      // publish this step's d_x and min-term operands; the barrier also
+      // waits for the stage loads.  The next weights are requested after it,
+      // so that the wait does not include them.
+      items_store(0, slot);
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < RB; ++b) load_raw<QT>(wr, wrow_off[b] + (uint32_t)((sb + 1) * BYTES), g4, raw[b]);
     }
 
     // integer contraction (two planes x four K chunks x RB row blocks) and
@@ -235,6 +255,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       if (t + 1 < TB) loadB(t + 1, Bn);
+      // keep the next block's fragment reads ahead of this block's MFMAs (the
+      // scheduler would otherwise sink each read next to its use and expose
+      // the LDS latency)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         v4i al = {0, 0, 0, 0}, ah = {0, 0, 0, 0};
@@ -250,6 +274,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
+      __builtin_amdgcn_sched_barrier(0);
     }
     flush(TB - 1, RB - 1, pl, ph);
 
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
             bmin_lo[b][j] = lo;
           }
         }
-        const int gbase = (it & 4);  // ring slots of this group: gbase .. gbase + 3
+        const int gbase = ONE ? 0 : (it & 4);  // ring slots of this group: gbase .. gbase + 3
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
           const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * AMS;
@@ -288,16 +313,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
         }
       }
     }
-    items_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
-    __syncthreads();
+    if constexpr (ONE) {
+      __syncthreads();  // every read of the stage done before the next fill
+    } else {
+      items_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
+      __syncthreads();
+    }
   };
 
   // ---- prologue: the first weights and activation stage are requested
   // first, so that their latency overlaps the pre-scale scan below.
 #pragma unroll
   for (int b = 0; b < RB; ++b) load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, raw[b]);
-  act_dma(s_act0, s0);
-  items_load(s0);
+  if constexpr (!ONE) {
+    act_dma(s_act0, s0);
+    items_load(s0);
+  }
 
   // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
   // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
@@ -327,10 +358,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && TB <= 5) ? 2 : 1) void k_qgemm
     for (int i = tid; i < 2 * AMLO; i += NTH) s_amin[i] = (_Float16)0.0f;
   }
   __syncthreads();
-  items_store(0, 0);
-  __syncthreads();
+  if constexpr (!ONE) {
+    items_store(0, 0);
+    __syncthreads();
+  }
 
-  if constexpr (RB == 1) {
+  if constexpr (ONE) {
+    for (int64_t sb = s0; sb < s1; ++sb) step(sb, s_act0, s_act0, 0);
+  } else if constexpr (RB == 1) {
     // two steps per iteration, each naming its stages directly
     int64_t sb = s0;
     for (; sb + 1 < s1; sb += 2) {
@@ -490,25 +525,25 @@ __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w,
 }
 
 // ---- host-side launch helpers -------------------------------------------
-template <int QT, int TB, int NW, int RB, bool ARGMAX>
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
 static hipError_t launch_k(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX>), grid, dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX, ST>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-template <int QT, int NW, int RB, bool ARGMAX>
+template <int QT, int NW, int RB, bool ARGMAX, int ST = 2>
 static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s) {
   switch (tb) {
-    case 1: return launch_k<QT, 1, NW, RB, ARGMAX>(p, grid, s);
-    case 2: return launch_k<QT, 2, NW, RB, ARGMAX>(p, grid, s);
-    case 3: return launch_k<QT, 3, NW, RB, ARGMAX>(p, grid, s);
-    case 4: return launch_k<QT, 4, NW, RB, ARGMAX>(p, grid, s);
-    case 5: return launch_k<QT, 5, NW, RB, ARGMAX>(p, grid, s);
-    case 6: return launch_k<QT, 6, NW, RB, ARGMAX>(p, grid, s);
-    case 7: return launch_k<QT, 7, NW, RB, ARGMAX>(p, grid, s);
-    case 8: return launch_k<QT, 8, NW, RB, ARGMAX>(p, grid, s);
-    case 9: return launch_k<QT, 9, NW, RB, ARGMAX>(p, grid, s);
-    default: return launch_k<QT, 10, NW, RB, ARGMAX>(p, grid, s);
+    case 1: return launch_k<QT, 1, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 2: return launch_k<QT, 2, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 3: return launch_k<QT, 3, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 4: return launch_k<QT, 4, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 5: return launch_k<QT, 5, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 6: return launch_k<QT, 6, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 7: return launch_k<QT, 7, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 8: return launch_k<QT, 8, NW, RB, ARGMAX, ST>(p, grid, s);
+    case 9: return launch_k<QT, 9, NW, RB, ARGMAX, ST>(p, grid, s);
+    default: return launch_k<QT, 10, NW, RB, ARGMAX, ST>(p, grid, s);
   }
 }
 
@@ -517,12 +552,15 @@ static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s
 //   cfg 2: 8 x 1 (128 rows), up to 160 tokens
 //   cfg 3: 8 x 2 (256 rows), up to 80 tokens
 //   cfg 4: 4 x 2 (128 rows), up to 80 tokens, two work-groups per CU
+//   cfg 5: 4 x 1 (64 rows), up to 160 tokens, one activation stage, two
+//          work-groups per CU
 // The LM head (argmax) uses cfg 1.
 template <int QT>
 static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (argmax) return launch_q<QT, 4, 1, true>(p, tb, grid, s);
   if (cfg == 1) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
   if (cfg == 2) return launch_q<QT, 8, 1, false>(p, tb, grid, s);
+  if (cfg == 5) return launch_q<QT, 4, 1, false, 1>(p, tb, grid, s);
   const bool c3 = (cfg == 3);
   switch (tb) {
     case 1: return c3 ? launch_k<QT, 1, 8, 2, false>(p, grid, s) : launch_k<QT, 1, 4, 2, false>(p, grid, s);
@@ -533,8 +571,8 @@ static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bo
   }
 }
 
-int qgemm_cfg_rows(int cfg) { return cfg == 1 ? 64 : (cfg == 3 ? 256 : 128); }
-int qgemm_cfg_max_tb(int cfg) { return cfg >= 3 ? 5 : 10; }
+int qgemm_cfg_rows(int cfg) { return (cfg == 1 || cfg == 5) ? 64 : (cfg == 3 ? 256 : 128); }
+int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4) ? 5 : 10; }
 
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);

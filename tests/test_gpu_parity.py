@@ -146,13 +146,13 @@ def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
 
 
 @pytest.mark.parametrize("qtype", [12, 14])
-@pytest.mark.parametrize("tile", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5"])
 @pytest.mark.parametrize("M,N,K", [(148, 333, 2048), (37, 130, 1024), (160, 256, 512)])
 def test_qgemm_every_tile_configuration(dl, monkeypatch, qtype, tile, M, N, K):
     """Each work-group shape (64 rows as 4 waves x 16, 128 rows as 8 waves x
     16, and over at most 80 tokens 256 rows as 8 waves x 32 or 128 rows as 4
-    waves x 32), pinned through DLLM_QGEMM_TILE, on ragged rows and tokens,
-    split and unsplit."""
+    waves x 32; 64 rows as 4 waves x 16 with one activation stage), pinned
+    through DLLM_QGEMM_TILE, on ragged rows and tokens, split and unsplit."""
     monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
     _say(f"qgemm tile={tile} qtype={qtype} M={M} N={N} K={K}")
     w = _weights(qtype, N, K, 11, f"t-{N}-{K}")
