@@ -269,6 +269,23 @@ def test_qgemm_deterministic(dl):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("qtype,N,K", [(12, 24576, 4096), (12, 12288, 4096), (12, 8192, 4096), (12, 4096, 4096),
+                                        (14, 4096, 4096), (12, 4096, 12288), (14, 4096, 12288)])
+def test_qgemm_step_shapes_at_148_tokens(dl, qtype, N, K):
+    """Every linear-layer shape of the LLaDA-8B step at L = 148, in the launch
+    configuration the step uses (tuned tile and K split, with workspace):
+    whole oracle rows for five tokens spread over both token tiles."""
+    M = 148
+    _say(f"step shape qtype={qtype} N={N} K={K}")
+    w = _weights(qtype, N, K, 21, f"step-{qtype}-{N}-{K}")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 21, f"step-x-{K}").numpy())
+    ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
+    y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    toks = [0, 63, 79, 80, 147]
+    ref = oracle.gemm(qtype, w.numpy(), N, K, xq[toks], len(toks))
+    assert_close_rows(y[toks], ref, f"step shape {qtype} {N}x{K}")
+
+
 def test_qgemm_shared_workspace_across_shapes(dl):
     """One workspace, sized for the largest, serves K-split calls of
     different shapes in stream order (whole oracle rows of four tokens)."""
