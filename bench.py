@@ -68,12 +68,13 @@ def profile_dominant(args):
     _, N, K = DOMINANT
     L = args.L
     w = synth.q4k_rows(N, K, args.seed, "L01.ffn_gate_up", dev)
-    xq = dl.quantize_q8k(synth.normal_f32((L, K), args.seed, "L01.h_norm", dev))
+    dmax = torch.empty(L, dtype=torch.float32, device=dev)
+    xq = dl.quantize_q8k(synth.normal_f32((L, K), args.seed, "L01.h_norm", dev), dmax=dmax)
     y = torch.empty((L, N), dtype=torch.float32, device=dev)
     ws = dl.qgemm_workspace(dl.Q4_K, N, K, L, dev)
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        dl.qgemm(dl.Q4_K, w, N, K, xq, L, y=y, workspace=ws)
+        dl.qgemm(dl.Q4_K, w, N, K, xq, L, y=y, workspace=ws, x_dmax=dmax)
     torch.cuda.synchronize()
     print(f"[profile-dominant] copy of {a.numel() * 4} bytes, then {args.steps} x qgemm Q4_K N={N} K={K} M={L}",
           flush=True)
@@ -130,6 +131,8 @@ def main():
 
     xq_d = torch.empty((L, D // 256 * 292), dtype=torch.uint8, device=dev)
     xq_f = torch.empty((L, FFN // 256 * 292), dtype=torch.uint8, device=dev)
+    dmax_d = torch.empty(L, dtype=torch.float32, device=dev)  # per-token largest |d|
+    dmax_f = torch.empty(L, dtype=torch.float32, device=dev)
     y_qkv = torch.empty((L, 3 * D), dtype=torch.float32, device=dev)
     y_o = torch.empty((L, D), dtype=torch.float32, device=dev)
     y_gu = torch.empty((L, 2 * FFN), dtype=torch.float32, device=dev)
@@ -147,30 +150,30 @@ def main():
     # ---------------- the step as a list of calls --------------------------
     calls = []  # (kind, fn, algorithmic bytes, int8 ops)
 
-    def add_quant(x, out):
+    def add_quant(x, out, dmax):
         M, K = x.shape
-        calls.append(("quantize_q8k", lambda: dl.quantize_q8k(x, out), M * K * 4 + M * K // 256 * 292, 0,
-                      ("quantize_q8k", M, K)))
+        calls.append(("quantize_q8k", lambda: dl.quantize_q8k(x, out, dmax),
+                      M * K * 4 + M * K // 256 * 292 + M * 4, 0, ("quantize_q8k", M, K)))
 
-    def add_gemm(q, w, N, K, xq, y):
+    def add_gemm(q, w, N, K, xq, dmax, y):
         byts = N * K // 256 * bb(q) + L * K // 256 * 292 + L * N * 4
         kind = "qgemm_q4k" if q == Q4 else "qgemm_q6k"
-        calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws), byts, 2 * L * N * K,
-                      (kind, N, K)))
+        calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws, x_dmax=dmax), byts,
+                      2 * L * N * K, (kind, N, K)))
 
     for lw in layers:
-        add_quant(lw["x_norm"], xq_d)
+        add_quant(lw["x_norm"], xq_d, dmax_d)
         if lw["even"]:
-            add_gemm(Q4, lw["qk"], 2 * D, D, xq_d, y_qkv[:, :2 * D])
-            add_gemm(Q6, lw["v"], D, D, xq_d, y_qkv[:, 2 * D:])
+            add_gemm(Q4, lw["qk"], 2 * D, D, xq_d, dmax_d, y_qkv[:, :2 * D])
+            add_gemm(Q6, lw["v"], D, D, xq_d, dmax_d, y_qkv[:, 2 * D:])
         else:
-            add_gemm(Q4, lw["qkv"], 3 * D, D, xq_d, y_qkv)
-        add_quant(lw["attn"], xq_d)
-        add_gemm(Q4, lw["o"], D, D, xq_d, y_o)
-        add_quant(lw["h_norm"], xq_d)
-        add_gemm(Q4, lw["gu"], 2 * FFN, D, xq_d, y_gu)
-        add_quant(lw["act"], xq_f)
-        add_gemm(Q6 if lw["even"] else Q4, lw["down"], D, FFN, xq_f, y_down)
+            add_gemm(Q4, lw["qkv"], 3 * D, D, xq_d, dmax_d, y_qkv)
+        add_quant(lw["attn"], xq_d, dmax_d)
+        add_gemm(Q4, lw["o"], D, D, xq_d, dmax_d, y_o)
+        add_quant(lw["h_norm"], xq_d, dmax_d)
+        add_gemm(Q4, lw["gu"], 2 * FFN, D, xq_d, dmax_d, y_gu)
+        add_quant(lw["act"], xq_f, dmax_f)
+        add_gemm(Q6 if lw["even"] else Q4, lw["down"], D, FFN, xq_f, dmax_f, y_down)
     lm_bytes = (MASKED * D * 4 + MASKED * D // 256 * 292 + VOCAB * D // 256 * bb(Q6)
                 + MASKED * VOCAB * 4 + MASKED * 4)
     calls.append(("lmhead_q6k", lambda: dl.lmhead_masked(Q6, w_out, VOCAB, D, hidden, rows, logits, amax, ws_lm),

@@ -49,10 +49,10 @@ def _load():
     sig = {
         "dllm_abi_version": (I, []),
         "dllm_last_error": (ctypes.c_char_p, []),
-        "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P]),
+        "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
         "dllm_decode_qk": (I, [I, P, I64, P, P]),
         "dllm_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
-        "dllm_qgemm": (I, [I, P, I64, I64, P, I64, P, I64, P, I64, P]),
+        "dllm_qgemm": (I, [I, P, I64, I64, P, P, I64, P, I64, P, I64, P]),
         "dllm_lmhead_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_lmhead_masked": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, I64, P]),
         "dllm_qgemm_partials_i32": (I, [I, P, I64, I64, P, I64, P, P]),
@@ -98,14 +98,19 @@ def block_bytes(qtype: int) -> int:
     return {Q4_K: Q4_K_BYTES, Q6_K: Q6_K_BYTES}.get(qtype, 0)
 
 
-def quantize_q8k(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """f32 [M, K] (row stride = ldx) -> Q8_K records uint8 [M, K/256*292]."""
+def quantize_q8k(x: torch.Tensor, out: torch.Tensor | None = None,
+                 dmax: torch.Tensor | None = None) -> torch.Tensor:
+    """f32 [M, K] (row stride = ldx) -> Q8_K records uint8 [M, K/256*292].
+    `dmax` (f32 [M], optional) receives each token's largest |d|, which
+    qgemm takes as `x_dmax`."""
     dev = _dev(x)
     assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
     M, K = x.shape
     if out is None:
         out = torch.empty((M, K // QK_K * Q8_K_BYTES), dtype=torch.uint8, device=dev)
-    _check(lib.dllm_quantize_q8k(_ptr(x), M, K, x.stride(0), _ptr(out), _stream(dev)))
+    if dmax is not None:
+        assert dmax.dtype == torch.float32 and dmax.is_contiguous() and dmax.numel() >= M
+    _check(lib.dllm_quantize_q8k(_ptr(x), M, K, x.stride(0), _ptr(out), _ptr(dmax), _stream(dev)))
     return out
 
 
@@ -131,15 +136,19 @@ def qgemm_workspace(qtype: int, N: int, K: int, M: int, device) -> torch.Tensor:
 
 
 def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: int,
-          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+          x_dmax: torch.Tensor | None = None) -> torch.Tensor:
     """y[M, N] (f32) = dequant(x_q8k) @ dequant(w)^T.  `y` may be a row-strided
-    view; `workspace` (uint8, >= qgemm_workspace_bytes) enables the K split."""
+    view; `workspace` (uint8, >= qgemm_workspace_bytes) enables the K split;
+    `x_dmax` (f32 [M], from quantize_q8k) spares the kernel its own scan."""
     dev = _dev(w)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     assert y.dtype == torch.float32 and y.stride(1) == 1
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.dllm_qgemm(qtype, _ptr(w), N, K, _ptr(x_q8k), M, _ptr(y), y.stride(0),
+    if x_dmax is not None:
+        assert x_dmax.dtype == torch.float32 and x_dmax.is_contiguous() and x_dmax.numel() >= M
+    _check(lib.dllm_qgemm(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(y), y.stride(0),
                           _ptr(workspace), wsb, _stream(dev)))
     return y
 

@@ -196,14 +196,16 @@ int dllm_abi_version(void) { return DLLM_ABI_VERSION; }
 
 const char* dllm_last_error(void) { return g_err; }
 
-int dllm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, void* y_q8k, void* stream) {
+int dllm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, void* y_q8k, float* dmax, void* stream) {
   if (!x || !y_q8k) return fail(DLLM_E_ARG, "dllm_quantize_q8k: null pointer (x=%p, y=%p)", (const void*)x, y_q8k);
   if (M <= 0 || K <= 0 || K % 256)
     return fail(DLLM_E_SHAPE, "dllm_quantize_q8k: need M > 0 and K a positive multiple of 256 (M=%lld, K=%lld)",
                 (long long)M, (long long)K);
   if (ldx < K) return fail(DLLM_E_ARG, "dllm_quantize_q8k: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
-  if (!aligned(x, 4) || !aligned(y_q8k, 4)) return fail(DLLM_E_ALIGN, "dllm_quantize_q8k: x and y must be 4-byte aligned");
-  return hip_status(launch_quantize_q8k(x, ldx, nullptr, M, K / 256, (uint8_t*)y_q8k, (hipStream_t)stream),
+  if (!aligned(x, 4) || !aligned(y_q8k, 4) || !aligned(dmax, 4))
+    return fail(DLLM_E_ALIGN, "dllm_quantize_q8k: x, y and dmax must be 4-byte aligned");
+  if (M > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "dllm_quantize_q8k: M=%lld exceeds 2^31-1", (long long)M);
+  return hip_status(launch_quantize_q8k(x, ldx, nullptr, M, K / 256, (uint8_t*)y_q8k, dmax, (hipStream_t)stream),
                     "dllm_quantize_q8k launch");
 }
 
@@ -238,13 +240,13 @@ static int check_gemm_args(const char* fn, int qtype, const void* w, int64_t N, 
   return DLLM_OK;
 }
 
-int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M, float* y, int64_t ldy,
-               void* workspace, int64_t workspace_bytes, void* stream) {
+int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax, int64_t M,
+               float* y, int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
   int rc = check_gemm_args("dllm_qgemm", qtype, w, N, K, x_q8k, M);
   if (rc) return rc;
   if (!y) return fail(DLLM_E_ARG, "dllm_qgemm: null output pointer");
   if (ldy < N) return fail(DLLM_E_ARG, "dllm_qgemm: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
-  if (!aligned(y, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm: y must be 4-byte aligned");
+  if (!aligned(y, 4) || !aligned(x_dmax, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm: y and x_dmax must be 4-byte aligned");
   Plan pl = plan_gemm(qtype, N, K, M, true);
   const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
   if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
@@ -252,6 +254,7 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
   GemmParams p;
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
+  p.dmax = x_dmax;
   p.keys = nullptr;
   p.N = N;
   p.SB = K / 256;
@@ -320,7 +323,8 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   const int64_t SB = K / 256;
   uint8_t* xq = (uint8_t*)workspace;
   uint64_t* keys = (uint64_t*)((uint8_t*)workspace + align256(n_rows * SB * Q8K_BYTES));
-  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, s), "dllm_lmhead_masked gather/quantize launch")))
+  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, nullptr, s),
+                       "dllm_lmhead_masked gather/quantize launch")))
     return rc;
   if (lmhead_stream_fits(K, n_rows) && !lmhead_force_tiled()) {
     LmParams lp;
@@ -339,6 +343,7 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   GemmParams p;
   p.w = (const uint8_t*)w;
   p.xq = xq;
+  p.dmax = nullptr;
   p.out = logits;
   p.keys = keys;
   p.N = N;

@@ -9,6 +9,7 @@ namespace dllm {
 struct GemmParams {
   const uint8_t* w;
   const uint8_t* xq;
+  const float* dmax;     // per token, the largest |d| of its blocks, or null
   float* out;            // y (no split) or split partials
   uint64_t* keys;        // argmax keys [n_tiles][M] (LM head) or null
   int64_t N, SB, M;
@@ -29,7 +30,7 @@ struct LmParams {
 };
 
 hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
-                               hipStream_t s);
+                               float* dmax, hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
 // cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
 // 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up

@@ -331,19 +331,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   }
 
   // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
-  // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.
+  // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.  It comes
+  // from the token's largest |d| over the whole row: given by the caller, or
+  // else found by reading every block's d (one cache line per block).
   if (tid < TOK) {
     float esc = 1.0f;
     if constexpr (MINS) {
-      // sixteen independent loads in flight per round
       float mx = 0.0f;
-      const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
-      for (int64_t sb = s0; sb < s1; sb += 16) {
-        float v[16];
+      if (p.dmax) {
+        if (m0 + tid < M) mx = p.dmax[m0 + tid];
+      } else {
+        // sixteen independent loads in flight per round
+        const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
+        for (int64_t sb = 0; sb < SB; sb += 16) {
+          float v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
+          for (int u = 0; u < 16; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
 #pragma unroll
-        for (int u = 0; u < 16; ++u) mx = (sb + u < s1) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
+          for (int u = 0; u < 16; ++u) mx = (sb + u < SB) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
+        }
       }
       if (mx > 0.0f) {
         int e = 0;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     s_esc[tid] = esc;
   }
   if constexpr (MINS) {
-    for (int i = tid; i < 2 * AMLO; i += NTH) s_amin[i] = (_Float16)0.0f;
+    for (int i = tid; i < 2 * AMLO / 8; i += NTH) ((v4u*)s_amin)[i] = v4u{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   if constexpr (!ONE) {

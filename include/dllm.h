@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 1
+#define DLLM_ABI_VERSION 2
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -65,10 +65,12 @@ const char *dllm_last_error(void);
  * q = 0, bsums = 0.  Inputs must be finite.
  *   x      f32 [M][ldx], 4-byte aligned, ldx >= K
  *   y_q8k  [M][K/256] records of 292 bytes, 4-byte aligned (written)
+ *   dmax   optional f32 [M] (NULL: not written): per token, the largest |d|
+ *          over its K/256 records; dllm_qgemm takes it as x_dmax
  * The output is bit-identical to the format definition.
  */
 int dllm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
-                      void *y_q8k, void *stream);
+                      void *y_q8k, float *dmax, void *stream);
 
 /*
  * Decode Q4_K / Q6_K super-blocks into the shared form both types reduce to
@@ -91,6 +93,11 @@ int dllm_decode_qk(int qtype, const void *w, int64_t n_superblocks,
  *   qtype   DLLM_Q4_K or DLLM_Q6_K
  *   w       [N][K/256] weight super-blocks, 4-byte aligned
  *   x_q8k   [M][K/256] Q8_K records (from dllm_quantize_q8k), 4-byte aligned
+ *   x_dmax  optional f32 [M]: per token, the largest |d| over its records, as
+ *           written by dllm_quantize_q8k (NULL: the kernel reads every
+ *           record's d itself, which costs a few microseconds per call).
+ *           Only Q4_K uses it, for the power-of-two range scale of its min
+ *           term; the result is bit-identical with or without it.
  *   y       f32 [M][ldy], ldy >= N, 4-byte aligned (written, not accumulated)
  *   workspace / workspace_bytes   optional scratch for splitting K across
  *           work-groups; NULL/0 runs without a split.  A split needs
@@ -100,8 +107,9 @@ int dllm_decode_qk(int qtype, const void *w, int64_t n_superblocks,
  */
 int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M);
 int dllm_qgemm(int qtype, const void *w, int64_t N, int64_t K,
-               const void *x_q8k, int64_t M, float *y, int64_t ldy,
-               void *workspace, int64_t workspace_bytes, void *stream);
+               const void *x_q8k, const float *x_dmax, int64_t M, float *y,
+               int64_t ldy, void *workspace, int64_t workspace_bytes,
+               void *stream);
 
 /*
  * Masked-row LM head (Development plan, "Compute design", last bullet; README

@@ -41,7 +41,7 @@ FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails va
 
 
 def test_unsupported_type_message(dl):
-    rc = dl.lib.dllm_qgemm(8, FAKE, 64, 256, FAKE, 4, FAKE, 64, None, 0, None)
+    rc = dl.lib.dllm_qgemm(8, FAKE, 64, 256, FAKE, None, 4, FAKE, 64, None, 0, None)
     assert rc == dl.E_UNSUPPORTED
     msg = dl.last_error()
     assert "Q8_0" in msg and "Q4_K and Q6_K" in msg
@@ -49,37 +49,40 @@ def test_unsupported_type_message(dl):
 
 @pytest.mark.parametrize("K", [0, 100, 257, -256])
 def test_k_must_be_multiple_of_256(dl, K):
-    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, K, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
-    assert dl.lib.dllm_quantize_q8k(FAKE, 4, K, max(K, 1), FAKE, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, K, FAKE, None, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_quantize_q8k(FAKE, 4, K, max(K, 1), FAKE, None, None) == dl.E_SHAPE
 
 
 def test_null_pointers(dl):
-    assert dl.lib.dllm_qgemm(dl.Q4_K, None, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ARG
+    assert dl.lib.dllm_qgemm(dl.Q4_K, None, 64, 256, FAKE, None, 4, FAKE, 64, None, 0, None) == dl.E_ARG
     assert "null" in dl.last_error()
-    assert dl.lib.dllm_qgemm(dl.Q6_K, FAKE, 64, 256, FAKE, 4, None, 64, None, 0, None) == dl.E_ARG
-    assert dl.lib.dllm_quantize_q8k(None, 4, 256, 256, FAKE, None) == dl.E_ARG
+    assert dl.lib.dllm_qgemm(dl.Q6_K, FAKE, 64, 256, FAKE, None, 4, None, 64, None, 0, None) == dl.E_ARG
+    assert dl.lib.dllm_quantize_q8k(None, 4, 256, 256, FAKE, None, None) == dl.E_ARG
     assert dl.lib.dllm_decode_qk(dl.Q4_K, None, 1, FAKE, None) == dl.E_ARG
 
 
 def test_bad_shapes_and_leading_dims(dl):
-    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 0, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
-    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, 0, FAKE, 64, None, 0, None) == dl.E_SHAPE
-    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, 4, FAKE, 63, None, 0, None) == dl.E_ARG
-    assert dl.lib.dllm_quantize_q8k(FAKE, 4, 512, 500, FAKE, None) == dl.E_ARG
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 0, 256, FAKE, None, 4, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, None, 0, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, None, 4, FAKE, 63, None, 0, None) == dl.E_ARG
+    assert dl.lib.dllm_quantize_q8k(FAKE, 4, 512, 500, FAKE, None, None) == dl.E_ARG
     assert dl.lib.dllm_decode_qk(dl.Q6_K, FAKE, 0, FAKE, None) == dl.E_SHAPE
 
 
 def test_alignment(dl):
     odd = ctypes.c_void_p((1 << 20) + 8)  # 8-byte aligned, not 16
-    assert dl.lib.dllm_qgemm(dl.Q4_K, odd, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
+    assert dl.lib.dllm_qgemm(dl.Q4_K, odd, 64, 256, FAKE, None, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
     two = ctypes.c_void_p((1 << 20) + 2)
-    assert dl.lib.dllm_qgemm(dl.Q6_K, two, 64, 256, FAKE, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
-    assert dl.lib.dllm_quantize_q8k(two, 4, 256, 256, FAKE, None) == dl.E_ALIGN
+    assert dl.lib.dllm_qgemm(dl.Q6_K, two, 64, 256, FAKE, None, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
+    assert dl.lib.dllm_quantize_q8k(two, 4, 256, 256, FAKE, None, None) == dl.E_ALIGN
+    # the optional per-token scale summary must be 4-byte aligned too
+    assert dl.lib.dllm_quantize_q8k(FAKE, 4, 256, 256, FAKE, two, None) == dl.E_ALIGN
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 64, 256, FAKE, two, 4, FAKE, 64, None, 0, None) == dl.E_ALIGN
 
 
 def test_oversized_operands_rejected(dl):
     # 2 GiB of Q4_K weights: the kernels address operands with 32-bit offsets
-    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 1 << 20, 4096 * 4, FAKE, 4, FAKE, 1 << 20, None, 0, None) == dl.E_SHAPE
+    assert dl.lib.dllm_qgemm(dl.Q4_K, FAKE, 1 << 20, 4096 * 4, FAKE, None, 4, FAKE, 1 << 20, None, 0, None) == dl.E_SHAPE
     assert "2 GiB" in dl.last_error()
 
 

@@ -59,6 +59,12 @@ def _weights(qtype, N, K, seed, name):
     return synth.qk_rows(qtype, N, K, seed, name)
 
 
+def _dmax(xq: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Per token, the largest |d| over its Q8_K records (f32, exact)."""
+    d = np.ascontiguousarray(xq.reshape(M, K // 256, 292)[:, :, :4]).view("<f4")[..., 0]
+    return np.abs(d).max(axis=1).astype(np.float32)
+
+
 # ---------------------------------------------------------------- Q8_K ----
 @pytest.mark.parametrize("M,K,pad", [(1, 256, 0), (17, 512, 0), (148, 4096, 0), (148, 12288, 0), (33, 1024, 64)])
 def test_quantize_q8k_bitexact(dl, M, K, pad):
@@ -66,8 +72,10 @@ def test_quantize_q8k_bitexact(dl, M, K, pad):
     x = synth.normal_f32((M, K + pad), 11, f"q8k-{M}-{K}")
     x = x * torch.logspace(-3, 3, M).unsqueeze(1)  # spread of magnitudes
     ref = oracle.quantize_q8k(x[:, :K].numpy())
-    got = dl.quantize_q8k(x.to(DEV)[:, :K]).cpu().numpy()
+    dmax = torch.full((M,), -1.0, device=DEV)
+    got = dl.quantize_q8k(x.to(DEV)[:, :K], dmax=dmax).cpu().numpy()
     assert np.array_equal(got, ref)
+    assert np.array_equal(dmax.cpu().numpy(), _dmax(ref, M, K))
 
 
 def test_quantize_q8k_edge_blocks(dl):
@@ -82,8 +90,11 @@ def test_quantize_q8k_edge_blocks(dl):
     x[5, :] = synth.normal_f32((K,), 5, "edge")
     x[5, 256:512] = 0.0                        # an all-zero block inside a row
     ref = oracle.quantize_q8k(x.numpy())
-    got = dl.quantize_q8k(x.to(DEV)).cpu().numpy()
+    dmax = torch.full((6,), -1.0, device=DEV)
+    got = dl.quantize_q8k(x.to(DEV), dmax=dmax).cpu().numpy()
     assert np.array_equal(got, ref)
+    assert np.array_equal(dmax.cpu().numpy(), _dmax(ref, 6, K))
+    assert dmax[0].item() == 0.0  # an all-zero row
 
 
 def test_gather_quantize_through_lmhead_equals_plain_quantize(dl):
@@ -280,10 +291,40 @@ def test_qgemm_step_shapes_at_148_tokens(dl, qtype, N, K):
     w = _weights(qtype, N, K, 21, f"step-{qtype}-{N}-{K}")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 21, f"step-x-{K}").numpy())
     ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
-    y = dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    wd, xd = w.to(DEV), torch.from_numpy(xq).to(DEV)
+    dmax = torch.from_numpy(_dmax(xq, M, K)).to(DEV)
+    y = dl.qgemm(qtype, wd, N, K, xd, M, workspace=ws, x_dmax=dmax)
     toks = [0, 63, 79, 80, 147]
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq[toks], len(toks))
-    assert_close_rows(y[toks], ref, f"step shape {qtype} {N}x{K}")
+    assert_close_rows(y.cpu().numpy()[toks], ref, f"step shape {qtype} {N}x{K}")
+    # the per-token scale summary only spares the kernel its own scan
+    y2 = dl.qgemm(qtype, wd, N, K, xd, M, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5"])
+def test_qgemm_dmax_hint_matches_scan(dl, monkeypatch, tile):
+    """Q4_K with the per-token largest |d| from dllm_quantize_q8k: the same
+    bits as without it (where the kernel reads every d itself), for every
+    tile configuration, split and unsplit, on ragged shapes, with magnitudes
+    spread over nine decades so the power-of-two range scale differs per
+    token."""
+    monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
+    N, K, M = 333, 3072, 150
+    _say(f"dmax hint tile={tile}")
+    w = _weights(12, N, K, 23, "hint").to(DEV)
+    x = synth.normal_f32((M, K), 23, "hint-x") * torch.logspace(-4, 5, M).unsqueeze(1)
+    dmax = torch.empty(M, device=DEV)
+    xq = dl.quantize_q8k(x.to(DEV), dmax=dmax)
+    ref = oracle.gemm(12, w.cpu().numpy(), N, K, xq.cpu().numpy(), M)
+    ws = dl.qgemm_workspace(12, N, K, M, DEV)
+    for workspace in (ws, None):
+        a = dl.qgemm(12, w, N, K, xq, M, workspace=workspace, x_dmax=dmax)
+        b = dl.qgemm(12, w, N, K, xq, M, workspace=workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        assert_close_rows(a.cpu().numpy(), ref, f"dmax hint tile {tile} ws={workspace is not None}")
 
 
 def test_qgemm_shared_workspace_across_shapes(dl):
