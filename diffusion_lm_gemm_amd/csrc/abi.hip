@@ -122,11 +122,11 @@ struct Tuned {
 };
 constexpr Tuned kTuned[] = {
     {12, 24576, 4096, 129, 160, 2, 1},  // gate + up
-    {12, 12288, 4096, 129, 160, 4, 1},  // Q + K + V
-    {12, 8192, 4096, 129, 160, 3, 4},   // Q + K (V in Q6_K)
+    {12, 12288, 4096, 129, 160, 2, 2},  // Q + K + V
+    {12, 8192, 4096, 129, 160, 2, 4},   // Q + K (V in Q6_K)
     {12, 4096, 4096, 129, 160, 4, 4},   // O
     {14, 4096, 4096, 129, 160, 5, 4},   // V
-    {12, 4096, 12288, 129, 160, 3, 8},  // down
+    {12, 4096, 12288, 129, 160, 2, 8},  // down
     {14, 4096, 12288, 129, 160, 5, 8},  // down
 };
 

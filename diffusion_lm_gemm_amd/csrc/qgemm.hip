@@ -41,9 +41,11 @@ namespace dllm {
 // Four-wave tiles of at most 80 tokens fit two work-groups per CU (two waves
 // per SIMD, each with its own barrier); larger tiles run one per CU.
 // ST = 2: the activation stage of the next super-block is loaded while this
-// one is used (double buffer, one barrier per step).  ST = 1: one stage,
-// loaded at the start of each step (two barriers per step); with 4 waves this
-// fits two work-groups per CU whose waits the other one's work fills.
+// one is used (double buffer, one barrier per step); with one row block per
+// wave the next block's weights are also unpacked during this one's MFMAs.
+// ST = 1: one stage, loaded at the start of each step (two barriers per
+// step); with 4 waves this fits two work-groups per CU whose waits the other
+// one's work fills.
 template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
   constexpr bool ONE = (ST == 1);
@@ -58,7 +60,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // wave-wide load; the stage is padded to TOKP rows so the loads fill it
   // exactly (the padding rows are loaded and never read).
   constexpr int TOKP = (TOK + 4 * NW - 1) / (4 * NW) * (4 * NW);
-  constexpr int DPW = TOKP * 16 / (64 * NW);
+  // Stage loads and d_x items are issued by the first LW waves only: with
+  // two waves per SIMD the second ones then start each step on the matrix
+  // cores instead of queueing behind the first ones' loads.
+  constexpr int LW = (!ONE && RB == 1 && NW == 8) ? NW / 2 : NW;
+  constexpr int NTHL = 64 * LW;
+  constexpr int DPW = TOKP * 16 / (64 * LW);
   // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
   // ring (two groups of four super-blocks) of min-term activation operands,
   // high halves [slot][token][8] f16 then low halves likewise: one group is
@@ -80,10 +87,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // a slot of its own past TOK, which nothing reads, so every store is
   // unconditional and has its own address.
   constexpr int NITEM = MINS ? TOK * 2 : TOK;
-  constexpr int IPT = (NITEM + NTH - 1) / NTH;  // items per thread
-  __shared__ float s_dx[ONE ? 1 : 2][TOK + IPT * NTH];
+  constexpr int IPT = (NITEM + NTHL - 1) / NTHL;  // items per thread
+  __shared__ float s_dx[ONE ? 1 : 2][TOK + IPT * NTHL];
   __shared__ float s_esc[TOK];
-  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTH - NITEM) + 8 : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTHL - NITEM) + 8 : 8];
   __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -116,6 +123,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   const uint32_t dma_tok0 = (uint32_t)((m0 + wv * DPW * 4 + (lane >> 4)) * SB * Q8K_BYTES) + 4;
   const uint32_t tok_step = (uint32_t)(4 * SB * Q8K_BYTES);
   auto act_dma = [&](uint8_t* stage, int64_t sb) {
+    if constexpr (LW < NW) {
+      if (wv >= LW) return;
+    }
     const uint32_t soff = (uint32_t)(sb * Q8K_BYTES);
 #pragma unroll
     for (int k = 0; k < DPW; ++k) {
@@ -129,9 +139,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   uint32_t idx_d[IPT];
   v4u idx_b[MINS ? IPT : 1];
   auto items_load = [&](int64_t sb) {
+    if constexpr (LW < NW) {
+      if (wv >= LW) return;
+    }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-      const int item = tid + k * NTH;
+      const int item = tid + k * NTHL;
       const int it_c = item < NITEM ? item : NITEM - 1;
       const int tok = MINS ? (it_c >> 1) : it_c;
       const uint32_t xoff = (uint32_t)(((m0 + tok) * SB + sb) * Q8K_BYTES);
@@ -140,9 +153,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     }
   };
   auto items_store = [&](int buf, int slot8) {
+    if constexpr (LW < NW) {
+      if (wv >= LW) return;
+    }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-      const int item = tid + k * NTH;
+      const int item = tid + k * NTHL;
       const bool live = item < NITEM;
       const int it_c = live ? item : NITEM - 1;
       const int tok = MINS ? (it_c >> 1) : it_c;
@@ -321,6 +337,123 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     }
   };
 
+  // Pipelined form (two stages, one row block per wave): the weights of the
+  // step's block were unpacked during the previous step; the next block's
+  // unpack runs chunk by chunk between this block's token tiles, where its
+  // VALU work issues beside the MFMAs, and its raw data is then refilled
+  // with the block after it.
+  struct AState {
+    v4i lo[4], hi[4];
+    float dsel[4];
+  };
+  AState A0, A1;
+  uint32_t mhn0 = 0u, mhn2 = 0u, mhn3 = 0u;
+  auto unpack_full = [&](int64_t ub, AState& A) {
+    const uint32_t boff = wrow_off[0] + (uint32_t)(ub * BYTES);
+    const float drow = unpack<QT>(raw[0], g4, boff & 3u, A.lo, A.hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A.dsel[i] = __shfl(drow, 4 * g4 + i);
+  };
+  auto step_pp = [&](int64_t sb, const uint8_t* act, uint8_t* act_next, int buf, AState& A, AState& An) {
+    const int it = (int)(sb - s0);
+    const int slot = it & 3;
+    const bool more = sb + 1 < s1;
+    act_dma(act_next, sb + 1);  // past the end: an unread stage
+    items_load(sb + 1);
+    const uint32_t noff = wrow_off[0] + (uint32_t)((sb + 1) * BYTES);  // the next block
+    uint32_t sc03 = 0u, sc47 = 0u, mn03, mn47;
+    if constexpr (MINS) {
+      q4k_scales(raw[0][1], raw[0][2], raw[0][3], sc03, sc47, mn03, mn47);
+      mhn0 = raw[0][0];
+      mhn2 = raw[0][2];
+      mhn3 = raw[0][3];
+    }
+    const float dnext = f16_bits_to_f32(MINS ? raw[0][0] : raw[0][RAW - 1]);
+    int bunit[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bunit[c] = 16 * (act_unit<QT>(c, g4) ^ r);
+    auto loadB = [&](int t, v4i(&dstB)[4]) {
+      const uint8_t* arow = act + (t * 16 + r) * ACT_ROW;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + bunit[c]);
+    };
+    float dxr[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) dxr[t] = s_dx[buf][t * 16 + r];
+    auto flush = [&](int t, const v4i& al, const v4i& ah) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = (ah[i] << SHIFT) + al[i];
+        yacc[0][t][i] += (float)a * (A.dsel[i] * dxr[t]);
+      }
+      asm volatile("" : "+v"(yacc[0][t]));
+    };
+    v4i Bc[4], Bn[4];
+    loadB(0, Bc);
+    v4i pl = {0, 0, 0, 0}, ph = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (t + 1 < TB) loadB(t + 1, Bn);
+      __builtin_amdgcn_sched_barrier(0);
+      v4i al = {0, 0, 0, 0}, ah = {0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        al = __builtin_amdgcn_mfma_i32_16x16x64_i8(A.lo[c], Bc[c], al, 0, 0, 0);
+        ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(A.hi[c], Bc[c], ah, 0, 0, 0);
+      }
+      if (t > 0) flush(t - 1, pl, ph);
+      pl = al;
+      ph = ah;
+      // the next block's chunks, spread over the tiles
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((c * TB) / 4 == t) unpack_chunk<QT>(raw[0], g4, noff & 3u, c, sc03, sc47, An.lo[c], An.hi[c]);
+      if (t == (3 * TB) / 4) load_raw<QT>(wr, noff + BYTES, g4, raw[0]);
+      if (t == TB - 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) An.dsel[i] = __shfl(dnext, 4 * g4 + i);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    flush(TB - 1, pl, ph);
+    if constexpr (MINS) {
+      if (slot == 3 || !more) {
+        v8h bmin_hi, bmin_lo;
+        const bool live = row_ok[0] && g4 <= slot;
+        uint32_t q03, q47, mn03, mn47;
+        q4k_scales(0u, live ? mh2[0] : 0u, live ? mh3[0] : 0u, q03, q47, mn03, mn47);
+        const float ndmin = -f16_bits_to_f32(live ? (mh0[0] >> 16) : 0u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t mb = (j < 4) ? mn03 : mn47;
+          _Float16 hi, lo;
+          split_f16(ndmin * (float)((mb >> (8 * (j & 3))) & 63u), hi, lo);
+          bmin_hi[j] = hi;
+          bmin_lo[j] = lo;
+        }
+        const int gbase = it & 4;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const _Float16* src = s_amin + ((gbase + g4) * TOK + t * 16 + r) * AMS;
+          const v8h ahv = *(const v8h*)src;
+          const v8h alv = *(const v8h*)(src + AMLO);
+          yacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, ahv, yacc[0][t], 0, 0, 0);
+          yacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_hi, alv, yacc[0][t], 0, 0, 0);
+          yacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bmin_lo, ahv, yacc[0][t], 0, 0, 0);
+        }
+      }
+      // the next block's min-term bytes, now that this group's are used
+      const bool mine = (((it + 1) & 3) == g4);
+      mh0[0] = mine ? mhn0 : mh0[0];
+      mh2[0] = mine ? mhn2 : mh2[0];
+      mh3[0] = mine ? mhn3 : mh3[0];
+    }
+    items_store(buf ^ 1, (it + 1) & 7);
+    __syncthreads();
+  };
+
   // ---- prologue: the first weights and activation stage are requested
   // first, so that their latency overlaps the pre-scale scan below.
 #pragma unroll
@@ -372,13 +505,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   if constexpr (ONE) {
     for (int64_t sb = s0; sb < s1; ++sb) step(sb, s_act0, s_act0, 0);
   } else if constexpr (RB == 1) {
-    // two steps per iteration, each naming its stages directly
+    // the first block is unpacked here (and its min-term bytes kept); then
+    // two steps per iteration, each naming its stages and weights directly
+    unpack_full(s0, A0);
+    if constexpr (MINS) {
+      const bool mine = (g4 == 0);
+      mh0[0] = mine ? raw[0][0] : 0u;
+      mh2[0] = mine ? raw[0][2] : 0u;
+      mh3[0] = mine ? raw[0][3] : 0u;
+    }
+    load_raw<QT>(wr, wrow_off[0] + (uint32_t)((s0 + 1) * BYTES), g4, raw[0]);
     int64_t sb = s0;
     for (; sb + 1 < s1; sb += 2) {
-      step(sb, s_act0, s_act1, 0);
-      step(sb + 1, s_act1, s_act0, 1);
+      step_pp(sb, s_act0, s_act1, 0, A0, A1);
+      step_pp(sb + 1, s_act1, s_act0, 1, A1, A0);
     }
-    if (sb < s1) step(sb, s_act0, s_act1, 0);
+    if (sb < s1) step_pp(sb, s_act0, s_act1, 0, A0, A1);
   } else {
     // one step per iteration (fewer live registers; the compiler then waits
     // for the stage loads before the step's first LDS read)

@@ -170,6 +170,46 @@ __device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int
   }
 }
 
+// The same unpacking one K chunk c (0..3) at a time, so that it can be spread
+// between matrix instructions: the two int8 planes of chunk c's 16x64 A
+// fragment.  Q4_K takes the block's scale bytes sc03/sc47 (q4k_scales of
+// raw[1..3]); Q6_K aligns the dwords it needs itself (soff 0 or 2).
+template <int QT>
+__device__ __forceinline__ void unpack_chunk(const uint32_t (&raw)[QTr<QT>::RAW], int g4, uint32_t soff, int c,
+                                             uint32_t sc03, uint32_t sc47, v4i& alo, v4i& ahi) {
+  const int h = c >> 1, n = c & 1;
+  uint32_t lo[4], hi[4];
+  if constexpr (QT == QT_Q4K) {
+    const int jb0 = 2 * (g4 >> 1);
+    const uint32_t scv = h ? sc47 : sc03;
+    const uint32_t sl = splat_byte_u16x2(scv & 0x07070707u, jb0 + n);
+    const uint32_t sh = splat_byte_u16x2((scv >> 3) & 0x07070707u, jb0 + n);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t v = raw[4 + 4 * h + d];
+      const uint32_t nib = n ? q4k_hi_nibbles(v) : q4k_lo_nibbles(v);
+      lo[d] = pkmul(nib, sl);
+      hi[d] = pkmul(nib, sh);
+    }
+  } else {
+    const uint32_t scd = __builtin_amdgcn_alignbyte(raw[20 + 2 * h + n + 1], raw[20 + 2 * h + n], soff);
+    const int s = (int)(int8_t)(scd >> (8 * g4));
+    const uint32_t s2 = ((uint32_t)(2 * s) & 0xFFFFu) * 0x10001u;
+    const uint32_t c64 = ((uint32_t)(-64 * s) & 0xFFFFu) * 0x10001u;
+    const int hsh = 2 * (2 * n + (g4 >> 1));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t ql = __builtin_amdgcn_alignbyte(raw[5 * h + d + 1], raw[5 * h + d], soff);
+      const uint32_t qh = __builtin_amdgcn_alignbyte(raw[10 + 5 * h + d + 1], raw[10 + 5 * h + d], soff);
+      const uint32_t lo4 = n ? q4k_hi_nibbles(ql) : q4k_lo_nibbles(ql);
+      const uint32_t hi2 = (qh >> hsh) & 0x03030303u;
+      q6_planes(lo4 | (hi2 << 4), s2, c64, lo[d], hi[d]);
+    }
+  }
+  alo = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+  ahi = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 __device__ __forceinline__ uint32_t f32_order_bits(float v) {
   if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
