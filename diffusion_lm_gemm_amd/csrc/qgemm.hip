@@ -702,11 +702,13 @@ static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s
 //   cfg 4: 4 x 2 (128 rows), up to 80 tokens, two work-groups per CU
 //   cfg 5: 4 x 1 (64 rows), up to 160 tokens, one activation stage, two
 //          work-groups per CU
+//   cfg 6: 4 x 1 (64 rows), up to 80 tokens, two work-groups per CU (the
+//          cfg 1 kernel on at most five token blocks)
 // The LM head (argmax) uses cfg 1.
 template <int QT>
 static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (argmax) return launch_q<QT, 4, 1, true>(p, tb, grid, s);
-  if (cfg == 1) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
+  if (cfg == 1 || cfg == 6) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
   if (cfg == 2) return launch_q<QT, 8, 1, false>(p, tb, grid, s);
   if (cfg == 5) return launch_q<QT, 4, 1, false, 1>(p, tb, grid, s);
   const bool c3 = (cfg == 3);
@@ -719,8 +721,8 @@ static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bo
   }
 }
 
-int qgemm_cfg_rows(int cfg) { return (cfg == 1 || cfg == 5) ? 64 : (cfg == 3 ? 256 : 128); }
-int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4) ? 5 : 10; }
+int qgemm_cfg_rows(int cfg) { return (cfg == 1 || cfg == 5 || cfg == 6) ? 64 : (cfg == 3 ? 256 : 128); }
+int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4 || cfg == 6) ? 5 : 10; }
 
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);
