@@ -108,8 +108,8 @@ struct Plan {
 // Time of one super-block step of a work-group with a full token tile, per
 // tile configuration, in microseconds, and its factor for Q6_K (heavier
 // unpacking), fitted to measured single-GEMM times on MI355X at 148 tokens.
-constexpr double kCfgStepUs[7] = {0.0, 2.610, 2.771, 2.748, 1.610, 1.871, 1.35};
-constexpr double kCfgQ6Factor[7] = {0.0, 0.873, 1.173, 1.864, 2.002, 1.039, 1.6};
+constexpr double kCfgStepUs[8] = {0.0, 2.610, 2.771, 2.748, 1.610, 1.871, 1.35, 2.4};
+constexpr double kCfgQ6Factor[8] = {0.0, 0.873, 1.173, 1.864, 2.002, 1.039, 1.6, 1.7};
 
 // Measured best (tile configuration, K split) for the linear layers of the
 // LLaDA-8B step (d = 4096, FFN 12288; Q4_K, and Q6_K for attn_v / ffn_down)
@@ -121,8 +121,8 @@ struct Tuned {
   int cfg, S;
 };
 constexpr Tuned kTuned[] = {
-    {12, 24576, 4096, 129, 160, 2, 1},  // gate + up
-    {12, 12288, 4096, 129, 160, 6, 1},  // Q + K + V
+    {12, 24576, 4096, 129, 160, 7, 1},  // gate + up
+    {12, 12288, 4096, 129, 160, 7, 2},  // Q + K + V
     {12, 8192, 4096, 129, 160, 6, 1},   // Q + K (V in Q6_K)
     {12, 4096, 4096, 129, 160, 6, 2},   // O
     {14, 4096, 4096, 129, 160, 5, 4},   // V
@@ -130,11 +130,11 @@ constexpr Tuned kTuned[] = {
     {14, 4096, 12288, 129, 160, 5, 8},  // down
 };
 
-// DLLM_QGEMM_TILE=1..6 pins the tile configuration (for testing every
+// DLLM_QGEMM_TILE=1..7 pins the tile configuration (for testing every
 // configuration on any shape); unset, the planner chooses.
 static int forced_cfg() {
   const char* e = getenv("DLLM_QGEMM_TILE");
-  if (!e || e[0] < '1' || e[0] > '6' || e[1]) return -1;
+  if (!e || e[0] < '1' || e[0] > '7' || e[1]) return -1;
   return e[0] - '0';
 }
 
@@ -158,7 +158,7 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
       return Plan{tb, t.cfg, cdiv(N, qgemm_cfg_rows(t.cfg)), cdiv(M, 16 * tb), S, (int)sps};
     }
   }
-  for (int cfg : {6, 5, 4, 3, 2, 1}) {
+  for (int cfg : {7, 6, 5, 4, 3, 2, 1}) {
     if (fc >= 0 && cfg != fc) continue;
     const int64_t rows = qgemm_cfg_rows(cfg);
     const int64_t n_tiles = cdiv(N, rows);

@@ -48,6 +48,7 @@ namespace dllm {
 // one's work fills.
 template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
+  static_assert(NW == 4 || NW == 8 || NW == 12, "waves per work-group: 4, 8 or 12 (whole SIMDs)");
   constexpr bool ONE = (ST == 1);
   constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
   constexpr int NTH = 64 * NW;          // threads
@@ -56,14 +57,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   constexpr int BYTES = QTr<QT>::BYTES;
   constexpr int RAW = QTr<QT>::RAW;
   constexpr bool MINS = (QT == QT_Q4K);
-  // buffer-to-LDS loads per wave per stage: 16 units per token, 64 units per
-  // wave-wide load; the stage is padded to TOKP rows so the loads fill it
-  // exactly (the padding rows are loaded and never read).
-  constexpr int TOKP = (TOK + 4 * NW - 1) / (4 * NW) * (4 * NW);
   // Stage loads and d_x items are issued by the first LW waves only: with
-  // two waves per SIMD the second ones then start each step on the matrix
+  // two or more waves per SIMD the others then start each step on the matrix
   // cores instead of queueing behind the first ones' loads.
-  constexpr int LW = (!ONE && RB == 1 && NW == 8) ? NW / 2 : NW;
+  constexpr int LW = (!ONE && RB == 1 && NW >= 8) ? 4 : NW;
+  // buffer-to-LDS loads per loading wave per stage: 16 units per token, 64
+  // units per wave-wide load; the stage is padded to TOKP rows so the loads
+  // fill it exactly (the padding rows are loaded and never read).
+  constexpr int TOKP = (TOK + 4 * LW - 1) / (4 * LW) * (4 * LW);
   constexpr int NTHL = 64 * LW;
   constexpr int DPW = TOKP * 16 / (64 * LW);
   // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
@@ -388,12 +389,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       }
       asm volatile("" : "+v"(yacc[0][t]));
     };
+    // with three waves per SIMD the others hide a tile's fragment reads, and
+    // the registers of a second fragment set are not there
+    constexpr bool BPRE = (NW < 12);
     v4i Bc[4], Bn[4];
-    loadB(0, Bc);
+    if constexpr (BPRE) loadB(0, Bc);
     v4i pl = {0, 0, 0, 0}, ph = {0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      if (t + 1 < TB) loadB(t + 1, Bn);
+      if constexpr (BPRE) {
+        if (t + 1 < TB) loadB(t + 1, Bn);
+      } else {
+        loadB(t, Bc);
+      }
       __builtin_amdgcn_sched_barrier(0);
       v4i al = {0, 0, 0, 0}, ah = {0, 0, 0, 0};
 #pragma unroll
@@ -413,8 +421,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
         for (int i = 0; i < 4; ++i) An.dsel[i] = __shfl(dnext, 4 * g4 + i);
       }
+      if constexpr (BPRE) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
+        for (int c = 0; c < 4; ++c) Bc[c] = Bn[c];
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     flush(TB - 1, pl, ph);
@@ -704,6 +714,7 @@ static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s
 //          work-groups per CU
 //   cfg 6: 4 x 1 (64 rows), up to 80 tokens, two work-groups per CU (the
 //          cfg 1 kernel on at most five token blocks)
+//   cfg 7: 12 x 1 (192 rows), up to 80 tokens (three waves per SIMD)
 // The LM head (argmax) uses cfg 1.
 template <int QT>
 static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
@@ -711,6 +722,15 @@ static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bo
   if (cfg == 1 || cfg == 6) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
   if (cfg == 2) return launch_q<QT, 8, 1, false>(p, tb, grid, s);
   if (cfg == 5) return launch_q<QT, 4, 1, false, 1>(p, tb, grid, s);
+  if (cfg == 7) {
+    switch (tb) {
+      case 1: return launch_k<QT, 1, 12, 1, false>(p, grid, s);
+      case 2: return launch_k<QT, 2, 12, 1, false>(p, grid, s);
+      case 3: return launch_k<QT, 3, 12, 1, false>(p, grid, s);
+      case 4: return launch_k<QT, 4, 12, 1, false>(p, grid, s);
+      default: return launch_k<QT, 5, 12, 1, false>(p, grid, s);
+    }
+  }
   const bool c3 = (cfg == 3);
   switch (tb) {
     case 1: return c3 ? launch_k<QT, 1, 8, 2, false>(p, grid, s) : launch_k<QT, 1, 4, 2, false>(p, grid, s);
@@ -721,8 +741,10 @@ static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bo
   }
 }
 
-int qgemm_cfg_rows(int cfg) { return (cfg == 1 || cfg == 5 || cfg == 6) ? 64 : (cfg == 3 ? 256 : 128); }
-int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4 || cfg == 6) ? 5 : 10; }
+int qgemm_cfg_rows(int cfg) {
+  return (cfg == 1 || cfg == 5 || cfg == 6) ? 64 : (cfg == 3 ? 256 : (cfg == 7 ? 192 : 128));
+}
+int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4 || cfg == 6 || cfg == 7) ? 5 : 10; }
 
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);

@@ -157,14 +157,15 @@ def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
 
 
 @pytest.mark.parametrize("qtype", [12, 14])
-@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6", "7"])
 @pytest.mark.parametrize("M,N,K", [(148, 333, 2048), (37, 130, 1024), (160, 256, 512)])
 def test_qgemm_every_tile_configuration(dl, monkeypatch, qtype, tile, M, N, K):
     """Each work-group shape (64 rows as 4 waves x 16, 128 rows as 8 waves x
     16, and over at most 80 tokens 256 rows as 8 waves x 32 or 128 rows as 4
     waves x 32; 64 rows as 4 waves x 16 with one activation stage; 64 rows as
-    4 waves x 16 over at most 80 tokens), pinned through DLLM_QGEMM_TILE, on
-    ragged rows and tokens, split and unsplit."""
+    4 waves x 16 over at most 80 tokens; 192 rows as 12 waves x 16 over at
+    most 80 tokens), pinned through DLLM_QGEMM_TILE, on ragged rows and
+    tokens, split and unsplit."""
     monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
     _say(f"qgemm tile={tile} qtype={qtype} M={M} N={N} K={K}")
     w = _weights(qtype, N, K, 11, f"t-{N}-{K}")
@@ -304,7 +305,7 @@ def test_qgemm_step_shapes_at_148_tokens(dl, qtype, N, K):
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6"])
+@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6", "7"])
 def test_qgemm_dmax_hint_matches_scan(dl, monkeypatch, tile):
     """Q4_K with the per-token largest |d| from dllm_quantize_q8k: the same
     bits as without it (where the kernel reads every d itself), for every
