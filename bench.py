@@ -309,7 +309,7 @@ def main():
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "qgemm.hip", "quantize.hip", "abi.hip"):
+    for f in ("common.hpp", "kernels.hpp", "unpack.hpp", "qgemm.hip", "quantize.hip", "abi.hip"):
         h.update(open(os.path.join(ROOT, "diffusion_lm_gemm_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
