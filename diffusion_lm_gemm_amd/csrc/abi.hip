@@ -130,6 +130,29 @@ constexpr Tuned kTuned[] = {
     {14, 4096, 12288, 129, 160, 5, 8},  // down
 };
 
+// DLLM_QGEMM_PLAN="qtype:N:K:cfg:S,..." replaces (or adds) tuned entries for
+// the listed shapes at any token count (for measuring alternatives in place).
+struct PlanOverride {
+  int qtype;
+  int64_t N, K;
+  int cfg, S;
+};
+static int plan_overrides(PlanOverride* out, int max_n) {
+  const char* e = getenv("DLLM_QGEMM_PLAN");
+  int n = 0;
+  while (e && *e && n < max_n) {
+    PlanOverride o;
+    long long q, nn, kk, c, s;
+    int used = 0;
+    if (sscanf(e, "%lld:%lld:%lld:%lld:%lld%n", &q, &nn, &kk, &c, &s, &used) != 5) break;
+    o.qtype = (int)q; o.N = nn; o.K = kk; o.cfg = (int)c; o.S = (int)s;
+    if (o.cfg >= 1 && o.cfg <= 7 && o.S >= 1 && o.S <= 16) out[n++] = o;
+    e += used;
+    if (*e == ',') ++e;
+  }
+  return n;
+}
+
 // DLLM_QGEMM_TILE=1..7 pins the tile configuration (for testing every
 // configuration on any shape); unset, the planner chooses.
 static int forced_cfg() {
@@ -148,6 +171,19 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   const int64_t SB = K / 256;
   const int fc = forced_cfg();
   if (fc < 0) {
+    PlanOverride ov[16];
+    const int nov = plan_overrides(ov, 16);
+    for (int i = 0; i < nov; ++i) {
+      const PlanOverride& o = ov[i];
+      if (o.qtype != qtype || o.N != N || o.K != K) continue;
+      const int S = allow_split ? o.S : 1;
+      const int64_t sps = cdiv(SB, S);
+      const int max_tb = qgemm_cfg_max_tb(o.cfg);
+      const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
+      const int64_t n_tiles = cdiv(N, qgemm_cfg_rows(o.cfg)), m_tiles = cdiv(M, 16 * tb);
+      if (cdiv(SB, sps) != S || (S > 1 && (S + 3) * M * N * 4 >= ((int64_t)1 << 32))) break;
+      return Plan{tb, o.cfg, n_tiles, m_tiles, S, (int)sps};
+    }
     for (const Tuned& t : kTuned) {
       if (t.qtype != qtype || t.N != N || t.K != K || M < t.m_lo || M > t.m_hi) continue;
       const int S = allow_split ? t.S : 1;

@@ -394,6 +394,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     constexpr bool BPRE = (NW < 12);
     v4i Bc[4], Bn[4];
     if constexpr (BPRE) loadB(0, Bc);
+    // the matrix loop runs at a raised wave priority, so that waves in it win
+    // issue slots over waves doing staging work
+    __builtin_amdgcn_s_setprio(1);
     v4i pl = {0, 0, 0, 0}, ph = {0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
@@ -428,6 +431,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       __builtin_amdgcn_sched_barrier(0);
     }
     flush(TB - 1, pl, ph);
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (MINS) {
       if (slot == 3 || !more) {
         v8h bmin_hi, bmin_lo;

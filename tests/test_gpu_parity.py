@@ -329,6 +329,21 @@ def test_qgemm_dmax_hint_matches_scan(dl, monkeypatch, tile):
         assert_close_rows(a.cpu().numpy(), ref, f"dmax hint tile {tile} ws={workspace is not None}")
 
 
+@pytest.mark.parametrize("plan", ["12:333:3072:7:4", "12:333:3072:6:3", "12:333:3072:2:12"])
+def test_qgemm_plan_override(dl, monkeypatch, plan):
+    """DLLM_QGEMM_PLAN pins (tile configuration, K split) for a shape; the
+    result stays within the bound for each pinned plan."""
+    monkeypatch.setenv("DLLM_QGEMM_PLAN", plan)
+    N, K, M = 333, 3072, 150
+    _say(f"plan override {plan}")
+    w = _weights(12, N, K, 29, "plan")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 29, "plan-x").numpy())
+    ref = oracle.gemm(12, w.numpy(), N, K, xq, M)
+    ws = dl.qgemm_workspace(12, N, K, M, DEV)
+    y = dl.qgemm(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
+    assert_close_rows(y, ref, f"plan {plan}")
+
+
 def test_qgemm_shared_workspace_across_shapes(dl):
     """One workspace, sized for the largest, serves K-split calls of
     different shapes in stream order (whole oracle rows of four tokens)."""
