@@ -8,7 +8,7 @@
 // synchronises its work-group once per super-block spends its time waiting
 // for weights.  Here every work-group loads the gathered Q8_K rows into LDS
 // once (all of K), and then each wave streams its own 16-row blocks with the
-// weights requested two super-blocks ahead and no barrier: one wave's memory
+// weights requested three super-blocks ahead and no barrier: one wave's memory
 // latency is covered by the others.  The arithmetic is the GEMM's (two int8
 // planes on v_mfma_i32_16x16x64_i8, the per-super-block f32 epilogue, and for
 // Q4_K the min term on f16 MFMA), and each wave keeps, per token, the largest
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
   uint32_t mh0 = 0, mh2 = 0, mh3 = 0;
   int64_t k = 0;   // row block index of this wave's stream
   int sb = 0;      // super-block within it
-  int64_t k2 = 0;  // the block two steps ahead
+  int64_t k2 = 0;  // the block three steps ahead
   int sb2 = 0;
   auto advance = [&](int64_t& kk, int& s) {
     if (++s == SB) { s = 0; ++kk; }
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
       mh2 = mine ? raw[2] : mh2;
       mh3 = mine ? raw[3] : mh3;
     }
-    // the block two steps ahead (past the end: reads nothing that is used)
+    // the block three steps ahead (past the end: reads nothing that is used)
     load_raw<QT>(wr, woff(k2, sb2), g4, raw);
     advance(k2, sb2);
     float dsel[4];
@@ -211,17 +211,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
     advance(k, sb);
   };
 
-  uint32_t rawA[RAW], rawB[RAW];
+  // three weight super-blocks in flight per wave: with two waves per SIMD
+  // that is what covers the memory latency of this stream
+  uint32_t rawA[RAW], rawB[RAW], rawC[RAW];
   load_raw<QT>(wr, woff(k2, sb2), g4, rawA);
   advance(k2, sb2);
   load_raw<QT>(wr, woff(k2, sb2), g4, rawB);
   advance(k2, sb2);
+  load_raw<QT>(wr, woff(k2, sb2), g4, rawC);
+  advance(k2, sb2);
   int64_t st = 0;
-  for (; st + 1 < n_steps; st += 2) {
+  for (; st + 2 < n_steps; st += 3) {
     step(rawA);
     step(rawB);
+    step(rawC);
   }
   if (st < n_steps) step(rawA);
+  if (st + 1 < n_steps) step(rawB);
 
   // per token: best key over the wave's rows (lanes of one token differ in g4)
 #pragma unroll

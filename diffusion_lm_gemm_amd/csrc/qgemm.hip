@@ -601,23 +601,39 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 }
 
 // Sum of the K-split partial tiles in split order (deterministic): each
-// thread owns four consecutive elements of the M x N partial tile and keeps
-// four slices' loads in flight.  The slices are read through a buffer
-// resource, so slices past S (and elements past M x N) read as zero.
+// thread owns four consecutive elements of the M x N partial tile.  The
+// slices are read through a buffer resource, so elements past M x N read as
+// zero.  SC > 0 fixes the number of slices at compile time, so that all of a
+// thread's loads are in flight together; SC == 0 takes S at run time, four
+// slices at a time.  VEC: the four elements are one 16-byte store (N and ldy
+// multiples of four, y 16-byte aligned); otherwise element stores, which
+// also handle a row change inside the four.
+template <int SC, bool VEC>
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int S, int64_t M,
                                                     int64_t N, float* __restrict__ y, int64_t ldy) {
+  if constexpr (SC > 0) S = SC;
   const int64_t MN = M * N;
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= MN) return;
   const rsrc_t r = make_rsrc(ws, (int64_t)S * MN * 4);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  if (e0 + 4 <= MN) {
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      v4u v[4];
+  if (VEC || e0 + 4 <= MN) {
+    if constexpr (SC > 0) {
+      v4u v[SC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)(s0 + u) * MN + e0) * 4));
+      for (int u = 0; u < SC; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)u * MN + e0) * 4));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc += __builtin_bit_cast(v4f, v[u]);
+      for (int u = 0; u < SC; ++u) acc += __builtin_bit_cast(v4f, v[u]);
+    } else {
+      int s0 = 0;
+      for (; s0 + 4 <= S; s0 += 4) {
+        v4u v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)(s0 + u) * MN + e0) * 4));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += __builtin_bit_cast(v4f, v[u]);
+      }
+      for (; s0 < S; ++s0) acc += __builtin_bit_cast(v4f, buf_ld128(r, (uint32_t)(((int64_t)s0 * MN + e0) * 4)));
     }
   } else {
     // the last, partial group of four: element loads (a 16-byte load that
@@ -628,10 +644,14 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
         acc[i] += __builtin_bit_cast(float, buf_ld32(r, (uint32_t)(((int64_t)s0 * MN + e0 + i) * 4)));
   }
   int64_t m = e0 / N, n = e0 - m * N;
+  if constexpr (VEC) {
+    *(v4f*)(y + m * ldy + n) = acc;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (e0 + i < MN) y[m * ldy + n] = acc[i];
-    if (++n == N) { n = 0; ++m; }
+    for (int i = 0; i < 4; ++i) {
+      if (e0 + i < MN) y[m * ldy + n] = acc[i];
+      if (++n == N) { n = 0; ++m; }
+    }
   }
 }
 
@@ -755,9 +775,25 @@ hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 gr
   return launch_cfg<QT_Q6K>(p, tb, cfg, grid, argmax, s);
 }
 
+template <bool VEC>
+static void launch_reduce_s(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
+  const dim3 grid((unsigned)((M * N + 1023) / 1024)), block(256);
+  switch (S) {
+    case 2: hipLaunchKernelGGL((k_split_reduce<2, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    case 3: hipLaunchKernelGGL((k_split_reduce<3, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    case 4: hipLaunchKernelGGL((k_split_reduce<4, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    case 6: hipLaunchKernelGGL((k_split_reduce<6, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    case 8: hipLaunchKernelGGL((k_split_reduce<8, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    default: hipLaunchKernelGGL((k_split_reduce<0, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+  }
+}
+
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
-  const int64_t total = M * N;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((total + 1023) / 1024)), dim3(256), 0, s, ws, S, M, N, y, ldy);
+  const bool vec = (N % 4 == 0) && (ldy % 4 == 0) && ((((uintptr_t)y) & 15) == 0);
+  if (vec)
+    launch_reduce_s<true>(ws, S, M, N, y, ldy, s);
+  else
+    launch_reduce_s<false>(ws, S, M, N, y, ldy, s);
   return hipGetLastError();
 }
 

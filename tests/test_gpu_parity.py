@@ -344,6 +344,29 @@ def test_qgemm_plan_override(dl, monkeypatch, plan):
     assert_close_rows(y, ref, f"plan {plan}")
 
 
+@pytest.mark.parametrize("N,pad,K,S", [(332, 0, 3072, 2), (332, 4, 3072, 3), (332, 0, 2560, 5), (332, 8, 3072, 6),
+                                       (332, 0, 4096, 8), (332, 0, 3072, 12), (333, 0, 3072, 4), (332, 1, 3072, 2),
+                                       (333, 3, 4096, 8), (333, 0, 2560, 5)])
+def test_qgemm_split_reduce_paths(dl, monkeypatch, N, pad, K, S):
+    """The K-split sum for fixed slice counts (2, 3, 4, 6, 8) and others (run
+    time), with 16-byte stores (N and the row stride multiples of four) and
+    element stores (either not), into a strided output whose padding columns
+    stay untouched."""
+    M = 150
+    monkeypatch.setenv("DLLM_QGEMM_PLAN", f"12:{N}:{K}:6:{S}")
+    assert dl.qgemm_workspace_bytes(12, N, K, M) == S * M * N * 4  # the pinned split is taken
+    _say(f"split reduce N={N} pad={pad} S={S}")
+    w = _weights(12, N, K, 31, f"red-{N}")
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 31, "red-x").numpy())
+    ref = oracle.gemm(12, w.numpy(), N, K, xq, M)
+    ws = dl.qgemm_workspace(12, N, K, M, DEV)
+    big = torch.full((M, N + pad), 7.0, device=DEV)
+    dl.qgemm(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, y=big[:, :N], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == 7.0)
+    assert_close_rows(big[:, :N].cpu().numpy(), ref, f"split reduce N={N} pad={pad} S={S}")
+
+
 def test_qgemm_shared_workspace_across_shapes(dl):
     """One workspace, sized for the largest, serves K-split calls of
     different shapes in stream order (whole oracle rows of four tokens)."""
