@@ -675,7 +675,9 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restr
 }
 
 // Test export: per-16 integer partial dots of the unsigned shared-form quants
-// with the Q8_K quants, through the same bit unpacking as the GEMM.
+// with the Q8_K quants, with the quants taken from the GGUF bit layout by the
+// shared nibble and field helpers (the GEMM's fragment unpacking produces the
+// same quants in its own K order).
 template <int QT>
 __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w, int64_t N, int64_t SB,
                                                 const uint8_t* __restrict__ xq, int64_t M,

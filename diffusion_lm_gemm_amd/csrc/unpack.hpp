@@ -110,6 +110,26 @@ __device__ __forceinline__ void q6_planes(uint32_t q, uint32_t s2, uint32_t c64,
   lo = __builtin_amdgcn_perm(wo, we, 0x06020400u) >> 1;
 }
 
+// Q6_K: the four 6-bit quants of one dword for K chunk nibble N: the N-nibbles
+// of the low-bit bytes ql with, at bits 4..5, the 2-bit field of quarter
+// k = 2N + (g4 >> 1) of the high-bit bytes qh (bits 2k..2k+1 of each byte).
+// The field is shifted into place whole-dword and masked with the nibbles in
+// one and-or; what a shift carries in from a neighbouring byte is masked off.
+template <int N>
+__device__ __forceinline__ uint32_t q6_quants(uint32_t ql, uint32_t qh, int g4) {
+  const int k2 = 2 * (g4 >> 1);
+  if constexpr (N == 0) return ((qh << (4 - k2)) & 0x30303030u) | (ql & 0x0F0F0F0Fu);
+  else return ((qh >> k2) & 0x30303030u) | ((ql >> 4) & 0x0F0F0F0Fu);
+}
+
+// Q6_K: the signed scale of K chunk (h, n) for this lane's row and the u16x2
+// splats of 2s and -64s (q6_planes' factor and addend).
+__device__ __forceinline__ void q6_scale(uint32_t scd, int g4, uint32_t& s2, uint32_t& c64) {
+  const int sc = (int)(int8_t)(scd >> (8 * g4));
+  s2 = __builtin_amdgcn_perm(0u, (uint32_t)(2 * sc), 0x01000100u);
+  c64 = __builtin_amdgcn_perm(0u, (uint32_t)(-64 * sc), 0x01000100u);
+}
+
 // Unpack raw bytes into the two int8 planes of the four 16x64 A fragments
 // (K order of act_unit) and return the super-block factor d.  soff: the byte
 // offset of the block mod 4 (Q6_K only: 0 or 2).
@@ -152,16 +172,13 @@ __device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int
     for (int c = 0; c < 4; ++c) {
       const int h = c >> 1, n = c & 1;
       // scale index 8h + 4n + g4: byte g4 of scale dword 2h + n
-      const int s = (int)(int8_t)(sc[2 * h + n] >> (8 * g4));
-      const uint32_t s2 = ((uint32_t)(2 * s) & 0xFFFFu) * 0x10001u;
-      const uint32_t c64 = ((uint32_t)(-64 * s) & 0xFFFFu) * 0x10001u;
-      const int hsh = 2 * (2 * n + (g4 >> 1));  // high bits of quarter k = 2n + (g4 >> 1)
+      uint32_t s2, c64;
+      q6_scale(sc[2 * h + n], g4, s2, c64);
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t lo4 = n ? q4k_hi_nibbles(ql[h][d]) : q4k_lo_nibbles(ql[h][d]);
-        const uint32_t hi2 = (qh[h][d] >> hsh) & 0x03030303u;
-        q6_planes(lo4 | (hi2 << 4), s2, c64, lo[d], hi[d]);
+        const uint32_t q = n ? q6_quants<1>(ql[h][d], qh[h][d], g4) : q6_quants<0>(ql[h][d], qh[h][d], g4);
+        q6_planes(q, s2, c64, lo[d], hi[d]);
       }
       alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
       ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -193,17 +210,14 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&raw)[QTr<QT>::RAW]
     }
   } else {
     const uint32_t scd = __builtin_amdgcn_alignbyte(raw[20 + 2 * h + n + 1], raw[20 + 2 * h + n], soff);
-    const int s = (int)(int8_t)(scd >> (8 * g4));
-    const uint32_t s2 = ((uint32_t)(2 * s) & 0xFFFFu) * 0x10001u;
-    const uint32_t c64 = ((uint32_t)(-64 * s) & 0xFFFFu) * 0x10001u;
-    const int hsh = 2 * (2 * n + (g4 >> 1));
+    uint32_t s2, c64;
+    q6_scale(scd, g4, s2, c64);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const uint32_t ql = __builtin_amdgcn_alignbyte(raw[5 * h + d + 1], raw[5 * h + d], soff);
       const uint32_t qh = __builtin_amdgcn_alignbyte(raw[10 + 5 * h + d + 1], raw[10 + 5 * h + d], soff);
-      const uint32_t lo4 = n ? q4k_hi_nibbles(ql) : q4k_lo_nibbles(ql);
-      const uint32_t hi2 = (qh >> hsh) & 0x03030303u;
-      q6_planes(lo4 | (hi2 << 4), s2, c64, lo[d], hi[d]);
+      const uint32_t q = n ? q6_quants<1>(ql, qh, g4) : q6_quants<0>(ql, qh, g4);
+      q6_planes(q, s2, c64, lo[d], hi[d]);
     }
   }
   alo = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
