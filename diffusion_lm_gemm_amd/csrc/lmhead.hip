@@ -29,6 +29,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
   constexpr int RAW = QTr<QT>::RAW;
+  constexpr int RAWW = QTw<QT>::RAW;  // dword-aligned loads (see load_raw_dw)
   constexpr bool MINS = (QT == QT_Q4K);
   constexpr int NTH = 64 * NW;
   // activations, natural K order per token, 16-byte units XOR-swizzled by
@@ -121,10 +122,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
     if (++s == SB) { s = 0; ++kk; }
   };
 
-  auto step = [&](uint32_t(&raw)[RAW]) {
+  auto step = [&](uint32_t(&rw)[RAWW]) {
+    uint32_t raw[RAW];
+    align_raw<QT>(rw, woff(k, sb), raw);
     v4i alo[4], ahi[4];
-    const uint32_t boff = woff(k, sb);
-    const float drow = unpack<QT>(raw, g4, boff & 3u, alo, ahi);
+    const float drow = unpack<QT>(raw, g4, alo, ahi);
     if constexpr (MINS) {
       const bool mine = ((sb & 3) == g4);
       mh0 = mine ? raw[0] : mh0;
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
       mh3 = mine ? raw[3] : mh3;
     }
     // the block three steps ahead (past the end: reads nothing that is used)
-    load_raw<QT>(wr, woff(k2, sb2), g4, raw);
+    load_raw_dw<QT>(wr, woff(k2, sb2), g4, rw);
     advance(k2, sb2);
     float dsel[4];
 #pragma unroll
@@ -213,12 +215,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
 
   // three weight super-blocks in flight per wave: with two waves per SIMD
   // that is what covers the memory latency of this stream
-  uint32_t rawA[RAW], rawB[RAW], rawC[RAW];
-  load_raw<QT>(wr, woff(k2, sb2), g4, rawA);
+  uint32_t rawA[RAWW], rawB[RAWW], rawC[RAWW];
+  load_raw_dw<QT>(wr, woff(k2, sb2), g4, rawA);
   advance(k2, sb2);
-  load_raw<QT>(wr, woff(k2, sb2), g4, rawB);
+  load_raw_dw<QT>(wr, woff(k2, sb2), g4, rawB);
   advance(k2, sb2);
-  load_raw<QT>(wr, woff(k2, sb2), g4, rawC);
+  load_raw_dw<QT>(wr, woff(k2, sb2), g4, rawC);
   advance(k2, sb2);
   int64_t st = 0;
   for (; st + 2 < n_steps; st += 3) {

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const uint32_t boff = wrow_off[b] + (uint32_t)(sb * BYTES);
-      const float drow = unpack<QT>(raw[b], g4, boff & 3u, alo[b], ahi[b]);
+      const float drow = unpack<QT>(raw[b], g4, alo[b], ahi[b]);
       if constexpr (MINS) {
         const bool mine = (slot == g4);
         mh0[b] = mine ? raw[b][0] : mh0[b];
@@ -349,9 +349,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   };
   AState A0, A1;
   uint32_t mhn0 = 0u, mhn2 = 0u, mhn3 = 0u;
-  auto unpack_full = [&](int64_t ub, AState& A) {
-    const uint32_t boff = wrow_off[0] + (uint32_t)(ub * BYTES);
-    const float drow = unpack<QT>(raw[0], g4, boff & 3u, A.lo, A.hi);
+  auto unpack_full = [&](AState& A) {
+    const float drow = unpack<QT>(raw[0], g4, A.lo, A.hi);
 #pragma unroll
     for (int i = 0; i < 4; ++i) A.dsel[i] = __shfl(drow, 4 * g4 + i);
   };
@@ -418,7 +417,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       // the next block's chunks, spread over the tiles
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if ((c * TB) / 4 == t) unpack_chunk<QT>(raw[0], g4, noff & 3u, c, sc03, sc47, An.lo[c], An.hi[c]);
+        if ((c * TB) / 4 == t) unpack_chunk<QT>(raw[0], g4, c, sc03, sc47, An.lo[c], An.hi[c]);
       if (t == (3 * TB) / 4) load_raw<QT>(wr, noff + BYTES, g4, raw[0]);
       if (t == TB - 1) {
 #pragma unroll
@@ -521,7 +520,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   } else if constexpr (RB == 1) {
     // the first block is unpacked here (and its min-term bytes kept); then
     // two steps per iteration, each naming its stages and weights directly
-    unpack_full(s0, A0);
+    unpack_full(A0);
     if constexpr (MINS) {
       const bool mine = (g4 == 0);
       mh0[0] = mine ? raw[0][0] : 0u;

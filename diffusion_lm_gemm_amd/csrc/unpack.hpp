@@ -29,7 +29,7 @@ template <>
 struct QTr<QT_Q6K> {
   static constexpr int BYTES = Q6K_BYTES;
   static constexpr int SHIFT = 7;
-  static constexpr int RAW = 26;
+  static constexpr int RAW = 21;
 };
 
 __device__ __forceinline__ uint32_t pkmul(uint32_t a, uint32_t b) {
@@ -54,14 +54,6 @@ __device__ __forceinline__ int act_unit(int c, int g4) {
   else return 8 * (c >> 1) + 4 * (c & 1) + g4;
 }
 
-// Five dwords at the dword-aligned byte offset a (16 bytes starting at a or
-// a + 2, see unpack).
-__device__ __forceinline__ void ld5(rsrc_t r, uint32_t a, uint32_t* d) {
-  const v4u v = buf_ld128(r, a);
-  d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-  d[4] = buf_ld32(r, a + 16);
-}
-
 // Raw (packed) bytes of the lane's part of one weight super-block at byte
 // offset `off` of the weight buffer.  Reads past the end of the buffer (rows
 // beyond N) return zeros, so padded rows contribute nothing.
@@ -82,19 +74,64 @@ __device__ __forceinline__ void load_raw(rsrc_t wr, uint32_t off, int g4, uint32
     }
   } else {
     // Blocks are 210 bytes, so a block starts at a dword boundary or two
-    // bytes past one; each 16-byte field is fetched as the five dwords that
-    // cover it and aligned when unpacked.  Fields: low-bit bytes 64h + 16 g4
-    // (h = 0, 1), high-bit bytes 128 + 32h + 16 (g4 & 1), the 16 scales at
-    // 192, and the f16 d at 208 (a 16-bit load: a dword there would reach
-    // past the end of the buffer for a dword-aligned last block, and the
-    // buffer's range check would zero all of it).
+    // bytes past one; the 16-byte loads take the fields at their byte
+    // offsets (buffer loads need no dword alignment).  Fields: low-bit bytes
+    // 64h + 16 g4 (h = 0, 1), high-bit bytes 128 + 32h + 16 (g4 & 1), the 16
+    // scales at 192, and the f16 d at 208 (a 16-bit load: a dword there would
+    // reach past the end of the buffer for the last block, and the buffer's
+    // range check would zero all of it).
+    const v4u f[5] = {buf_ld128(wr, off + 16 * g4), buf_ld128(wr, off + 64 + 16 * g4),
+                      buf_ld128(wr, off + 128 + 16 * (g4 & 1)), buf_ld128(wr, off + 160 + 16 * (g4 & 1)),
+                      buf_ld128(wr, off + 192)};
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[4 * k + i] = f[k][i];
+    raw[20] = buf_ld16(wr, off + 208);
+  }
+}
+
+// Dword-aligned form of the raw loads, for streams bound by memory latency
+// (where a 16-byte load two bytes past a dword boundary costs more than the
+// byte alignment afterwards): Q6_K fields as the five dwords that cover each,
+// brought to the load_raw layout by align_raw once the data has arrived.
+template <int QT>
+struct QTw {
+  static constexpr int RAW = (QT == QT_Q6K) ? 26 : QTr<QT>::RAW;
+};
+
+template <int QT>
+__device__ __forceinline__ void load_raw_dw(rsrc_t wr, uint32_t off, int g4, uint32_t (&w)[QTw<QT>::RAW]) {
+  if constexpr (QT == QT_Q4K) {
+    load_raw<QT>(wr, off, g4, w);
+  } else {
     const uint32_t a = off & ~3u;
-    ld5(wr, a + 16 * g4, raw);
-    ld5(wr, a + 64 + 16 * g4, raw + 5);
-    ld5(wr, a + 128 + 16 * (g4 & 1), raw + 10);
-    ld5(wr, a + 160 + 16 * (g4 & 1), raw + 15);
-    ld5(wr, a + 192, raw + 20);
-    raw[25] = buf_ld16(wr, off + 208);
+    const uint32_t fo[5] = {a + 16 * g4, a + 64 + 16 * g4, a + 128 + 16 * (g4 & 1), a + 160 + 16 * (g4 & 1), a + 192};
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const v4u v = buf_ld128(wr, fo[k]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[5 * k + i] = v[i];
+      w[5 * k + 4] = buf_ld32(wr, fo[k] + 16);
+    }
+    w[25] = buf_ld16(wr, off + 208);
+  }
+}
+
+// load_raw_dw data of a block at byte offset `off` -> the load_raw layout.
+template <int QT>
+__device__ __forceinline__ void align_raw(const uint32_t (&w)[QTw<QT>::RAW], uint32_t off,
+                                          uint32_t (&raw)[QTr<QT>::RAW]) {
+  if constexpr (QT == QT_Q4K) {
+#pragma unroll
+    for (int i = 0; i < QTr<QT>::RAW; ++i) raw[i] = w[i];
+  } else {
+    const uint32_t soff = off & 3u;
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[4 * k + i] = __builtin_amdgcn_alignbyte(w[5 * k + i + 1], w[5 * k + i], soff);
+    raw[20] = w[25];
   }
 }
 
@@ -131,11 +168,9 @@ __device__ __forceinline__ void q6_scale(uint32_t scd, int g4, uint32_t& s2, uin
 }
 
 // Unpack raw bytes into the two int8 planes of the four 16x64 A fragments
-// (K order of act_unit) and return the super-block factor d.  soff: the byte
-// offset of the block mod 4 (Q6_K only: 0 or 2).
+// (K order of act_unit) and return the super-block factor d.
 template <int QT>
-__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, uint32_t soff, v4i (&alo)[4],
-                                        v4i (&ahi)[4]) {
+__device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int g4, v4i (&alo)[4], v4i (&ahi)[4]) {
   if constexpr (QT == QT_Q4K) {
     uint32_t sc03, sc47, mn03, mn47;
     q4k_scales(raw[1], raw[2], raw[3], sc03, sc47, mn03, mn47);
@@ -159,40 +194,32 @@ __device__ __forceinline__ float unpack(const uint32_t (&raw)[QTr<QT>::RAW], int
     }
     return f16_bits_to_f32(raw[0]);
   } else {
-    uint32_t ql[2][4], qh[2][4], sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ql[0][i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], soff);
-      ql[1][i] = __builtin_amdgcn_alignbyte(raw[5 + i + 1], raw[5 + i], soff);
-      qh[0][i] = __builtin_amdgcn_alignbyte(raw[10 + i + 1], raw[10 + i], soff);
-      qh[1][i] = __builtin_amdgcn_alignbyte(raw[15 + i + 1], raw[15 + i], soff);
-      sc[i] = __builtin_amdgcn_alignbyte(raw[20 + i + 1], raw[20 + i], soff);
-    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int h = c >> 1, n = c & 1;
       // scale index 8h + 4n + g4: byte g4 of scale dword 2h + n
       uint32_t s2, c64;
-      q6_scale(sc[2 * h + n], g4, s2, c64);
+      q6_scale(raw[16 + 2 * h + n], g4, s2, c64);
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t q = n ? q6_quants<1>(ql[h][d], qh[h][d], g4) : q6_quants<0>(ql[h][d], qh[h][d], g4);
+        const uint32_t ql = raw[4 * h + d], qh = raw[8 + 4 * h + d];
+        const uint32_t q = n ? q6_quants<1>(ql, qh, g4) : q6_quants<0>(ql, qh, g4);
         q6_planes(q, s2, c64, lo[d], hi[d]);
       }
       alo[c] = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
       ahi[c] = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    return f16_bits_to_f32(raw[25]);
+    return f16_bits_to_f32(raw[20]);
   }
 }
 
 // The same unpacking one K chunk c (0..3) at a time, so that it can be spread
 // between matrix instructions: the two int8 planes of chunk c's 16x64 A
 // fragment.  Q4_K takes the block's scale bytes sc03/sc47 (q4k_scales of
-// raw[1..3]); Q6_K aligns the dwords it needs itself (soff 0 or 2).
+// raw[1..3]).
 template <int QT>
-__device__ __forceinline__ void unpack_chunk(const uint32_t (&raw)[QTr<QT>::RAW], int g4, uint32_t soff, int c,
+__device__ __forceinline__ void unpack_chunk(const uint32_t (&raw)[QTr<QT>::RAW], int g4, int c,
                                              uint32_t sc03, uint32_t sc47, v4i& alo, v4i& ahi) {
   const int h = c >> 1, n = c & 1;
   uint32_t lo[4], hi[4];
@@ -209,13 +236,11 @@ __device__ __forceinline__ void unpack_chunk(const uint32_t (&raw)[QTr<QT>::RAW]
       hi[d] = pkmul(nib, sh);
     }
   } else {
-    const uint32_t scd = __builtin_amdgcn_alignbyte(raw[20 + 2 * h + n + 1], raw[20 + 2 * h + n], soff);
     uint32_t s2, c64;
-    q6_scale(scd, g4, s2, c64);
+    q6_scale(raw[16 + 2 * h + n], g4, s2, c64);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t ql = __builtin_amdgcn_alignbyte(raw[5 * h + d + 1], raw[5 * h + d], soff);
-      const uint32_t qh = __builtin_amdgcn_alignbyte(raw[10 + 5 * h + d + 1], raw[10 + 5 * h + d], soff);
+      const uint32_t ql = raw[4 * h + d], qh = raw[8 + 4 * h + d];
       const uint32_t q = n ? q6_quants<1>(ql, qh, g4) : q6_quants<0>(ql, qh, g4);
       q6_planes(q, s2, c64, lo[d], hi[d]);
     }
