@@ -408,27 +408,30 @@ def _check_argmax(logits_gpu, am_gpu, ref_logits, ref_am, what):
 @pytest.mark.parametrize("qtype", [12, 14])
 @pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 7, 32, 40])
-def test_lmhead_small(dl, monkeypatch, qtype, tiled, n_rows):
+@pytest.mark.parametrize("K", [768, 1024, 2560])
+def test_lmhead_small(dl, monkeypatch, qtype, tiled, n_rows, K):
     """Both LM-head paths: the streaming kernel (<= 32 rows, K <= 4096) and
     the tiled GEMM (forced with DLLM_LMHEAD_TILED=1, and taken for 40 rows),
     on a vocabulary that is not a multiple of any tile (1000 rows) and K of
-    three super-blocks."""
+    3, 4 and 10 super-blocks (the stream's three-deep load rotation then
+    meets a row-block boundary at every phase)."""
     if tiled:
         monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
-    N, K, M = 1000, 768, 148
-    _say(f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows}")
+    N, M = 1000, 148
+    _say(f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows} K={K}")
     w = _weights(qtype, N, K, 13, f"lm-small-{qtype}")
     h = synth.normal_f32((M, K), 13, "lm-h")
     rows = synth.distinct_rows(n_rows, M, 13, f"rows-{n_rows}")
     ref, ref_am = oracle.lmhead(qtype, w.numpy(), N, K, h.numpy(), rows.numpy())
     logits, am = dl.lmhead_masked(qtype, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
     logits = logits.cpu().numpy(); am = am.cpu().numpy()
-    assert_close_rows(logits, ref, f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows}")
+    assert_close_rows(logits, ref, f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows} K={K}")
     _check_argmax(logits, am, ref, ref_am, f"lmhead n_rows={n_rows}")
 
 
-def test_lmhead_q4k_and_ragged_vocab(dl):
-    N, K, M = 777, 768, 50
+@pytest.mark.parametrize("K", [768, 1280])
+def test_lmhead_q4k_and_ragged_vocab(dl, K):
+    N, M = 777, 50
     w = _weights(12, N, K, 14, "lm-q4")
     h = synth.normal_f32((M, K), 14, "lm-q4h")
     rows = synth.distinct_rows(9, M, 14, "rows")
@@ -438,8 +441,9 @@ def test_lmhead_q4k_and_ragged_vocab(dl):
     _check_argmax(logits.cpu().numpy(), am.cpu().numpy(), ref, ref_am, "lmhead q4k")
 
 
-def test_lmhead_exact_tie_picks_lowest_index(dl):
-    N, K, M = 300, 256, 8
+@pytest.mark.parametrize("K", [256, 1024])
+def test_lmhead_exact_tie_picks_lowest_index(dl, K):
+    N, M = 300, 8
     w = _weights(14, N, K, 15, "tie")
     w[200] = w[77]
     w[250] = w[77]
