@@ -58,6 +58,7 @@ def lib():
         L.oracle_q6k_fields.argtypes = [P, P, P, P]
         for name, args in {
             "oracle_decode_rows": [I, P, I64, I64, P],
+            "oracle_softmax_stats": [P, I64, I64, P, P],
             "oracle_decode_shared": [I, P, I64, P],
             "oracle_quantize_q8k": [P, I64, I64, I64, P],
             "oracle_dequant_q8k": [P, I64, I64, P],
@@ -186,3 +187,16 @@ def lmhead(qtype: int, w, N: int, K: int, h: np.ndarray, rows, nthreads: int | N
     _check(lib().oracle_lmhead(qtype, _p(w), N, K, _p(h), M, h.shape[1], _p(rows), n,
                                _p(logits), _p(am), nt), "lmhead")
     return logits, am
+
+
+def softmax_stats(logits: np.ndarray):
+    """(f64 log-sum-exp [n_rows], f64 softmax probability of the argmax
+    [n_rows]) of each row of f64 logits: the greedy pick's confidence."""
+    lg = np.ascontiguousarray(logits, np.float64)
+    if lg.ndim == 1:
+        lg = lg[None, :]
+    n, N = lg.shape
+    lse = np.zeros(n, np.float64)
+    p = np.zeros(n, np.float64)
+    _check(lib().oracle_softmax_stats(_p(lg), n, N, _p(lse), _p(p)), "softmax_stats")
+    return lse, p

@@ -399,3 +399,25 @@ int oracle_lmhead(int qtype, const uint8_t *w, int64_t N, int64_t K,
   free(xq);
   return 0;
 }
+
+/* ---- confidence of the greedy pick ------------------------------------- */
+/* Per logit row (the masked positions of a step): the log-sum-exp of the
+ * row, lse = m + log(sum_n exp(l_n - m)) with m = max_n l_n, and the softmax
+ * probability of the argmax token, exp(m - lse) = 1 / sum_n exp(l_n - m).
+ * The pages list softmax, log-softmax and argmax among the sampling
+ * primitives and give LLaDA low-confidence remasking, whose confidence of a
+ * committed token is its softmax probability.  Sums in f64, ascending n. */
+int oracle_softmax_stats(const double *logits, int64_t n_rows, int64_t N, double *lse, double *p_argmax) {
+  if (N <= 0) return -1;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const double *l = logits + r * N;
+    double m = l[0];
+    for (int64_t n = 1; n < N; ++n)
+      if (l[n] > m) m = l[n];
+    double s = 0.0;
+    for (int64_t n = 0; n < N; ++n) s += exp(l[n] - m);
+    lse[r] = m + log(s);
+    p_argmax[r] = 1.0 / s;
+  }
+  return 0;
+}

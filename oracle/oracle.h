@@ -26,4 +26,6 @@ int oracle_partials(int qtype, const uint8_t *w, int64_t N, int64_t K,
 int oracle_lmhead(int qtype, const uint8_t *w, int64_t N, int64_t K,
                   const float *h, int64_t M, int64_t ldh, const int32_t *rows,
                   int64_t n_rows, double *logits, int32_t *argmax, int nthreads);
+int oracle_softmax_stats(const double *logits, int64_t n_rows, int64_t N,
+                         double *lse, double *p_argmax);
 #endif

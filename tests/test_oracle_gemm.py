@@ -8,6 +8,7 @@ y = W_hat X_hat^T of the dequantized operands.  Pinned by: exact rational
 brute force from values chosen before packing, an f32 library dot product, an
 integer special case, zero weights, and planted argmax rows.
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -199,3 +200,51 @@ def test_lmhead_planted_argmax_and_lowest_index_tie():
     _, am = oracle.lmhead(oracle.Q6_K, w, N, K, h, np.array([0, 1], np.int32))
     assert am[0] == 29
     assert am[1] == 13
+
+
+# ---- confidence of the greedy pick (log-sum-exp, softmax probability of the argmax)
+
+def test_softmax_stats_closed_forms():
+    """Equal logits: lse = c + ln N, p = 1/N.  One logit a above N-1 zeros:
+    lse = ln(N - 1 + e^a), p = e^a / (N - 1 + e^a); below them the argmax is a
+    zero and p = 1 / (N - 1 + e^a)."""
+    for N, c in ((1, 0.25), (7, -3.0), (126464, 12.5)):
+        lse, p = oracle.softmax_stats(np.full((1, N), c))
+        assert abs(lse[0] - (c + math.log(N))) <= 1e-12 * (1 + abs(c) + math.log(N))
+        assert abs(p[0] - 1.0 / N) <= 1e-12 / N
+    for N, a in ((5, 2.0), (1000, 7.5), (1000, -4.0)):
+        row = np.zeros(N)
+        row[N // 3] = a
+        lse, p = oracle.softmax_stats(row)
+        z = (N - 1) + math.exp(a)
+        assert abs(lse[0] - math.log(z)) <= 1e-12 * max(1.0, abs(math.log(z)))
+        want = math.exp(a) / z if a > 0 else 1.0 / z
+        assert abs(p[0] - want) <= 1e-12 * want
+
+
+def test_softmax_stats_shift_and_large_values():
+    """Adding c to every logit adds c to lse and leaves p unchanged, also for
+    logits near 1000 where exp without the max shift overflows."""
+    rng = np.random.default_rng(31)
+    row = rng.standard_normal(4096) * 3.0
+    lse0, p0 = oracle.softmax_stats(row)
+    for c in (-500.0, 1000.0, 1e5):
+        lse, p = oracle.softmax_stats(row + c)
+        assert np.isfinite(lse[0]) and np.isfinite(p[0])
+        assert abs(lse[0] - (lse0[0] + c)) <= 1e-10 * (abs(c) + abs(lse0[0]))
+        assert abs(p[0] - p0[0]) <= 1e-9 * p0[0]
+    lse, p = oracle.softmax_stats(np.array([[1000.0, 1001.0]]))
+    assert abs(lse[0] - (1001.0 + math.log1p(math.exp(-1.0)))) <= 1e-12 * 1001.0
+    assert abs(p[0] - 1.0 / (1.0 + math.exp(-1.0))) <= 1e-15
+
+
+def test_softmax_stats_against_scipy():
+    """scipy.special.logsumexp (an independent routine) on random rows of
+    several spreads; p = exp(max - lse) from its value."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(32)
+    lg = rng.standard_normal((6, 3000)) * np.array([0.01, 0.5, 1.0, 4.0, 20.0, 300.0])[:, None]
+    lse, p = oracle.softmax_stats(lg)
+    ref = logsumexp(lg, axis=1)
+    assert np.allclose(lse, ref, rtol=1e-13, atol=1e-12)
+    assert np.allclose(p, np.exp(lg.max(axis=1) - ref), rtol=1e-11, atol=0)
