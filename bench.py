@@ -245,6 +245,20 @@ def main():
     dms, dn, dbytes, dops = per[dom]
     dom_name = f"{dom[0]}_{dom[1]}x{dom[2]}"
     achieved = dbytes / (dms * 1e-3) / 1e9
+    # the LM head with the greedy pick's confidence (log-sum-exp and softmax
+    # probability of the argmax per masked row; not part of the step), timed
+    # the same way on the same inputs
+    lse = torch.empty(MASKED, dtype=torch.float32, device=dev)
+    p_am = torch.empty(MASKED, dtype=torch.float32, device=dev)
+    conf = lambda: dl.lmhead_confidence(Q6, w_out, VOCAB, D, hidden, rows, logits, amax, lse, p_am, ws_lm)
+    conf()
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in cev:
+        a.record()
+        conf()
+        b.record()
+    torch.cuda.synchronize()
+    conf_ms = sum(a.elapsed_time(b) for a, b in cev) / reps
     print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
     print(f"[bench] per-call shapes: " + json.dumps(shapes), file=sys.stderr, flush=True)
 
@@ -300,6 +314,9 @@ def main():
                           for k, v in kinds.items()},
         "per_call_shape": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                            for k, v in shapes.items()},
+        "lmhead_confidence": {"avg_ms": round(conf_ms, 5), "GBps": round(lm_bytes / (conf_ms * 1e-3) / 1e9, 1),
+                              "outputs": "logits, argmax, log-sum-exp and p(argmax) per masked row",
+                              "in_step": False},
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),
     }

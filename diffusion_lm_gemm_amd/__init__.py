@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libdllm.so")
 HEADER_EXPORTS = (
     "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_decode_qk",
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_lmhead_workspace_bytes",
-    "dllm_lmhead_masked", "dllm_qgemm_partials_i32",
+    "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
 )
 
 
@@ -55,6 +55,7 @@ def _load():
         "dllm_qgemm": (I, [I, P, I64, I64, P, P, I64, P, I64, P, I64, P]),
         "dllm_lmhead_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_lmhead_masked": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, I64, P]),
+        "dllm_lmhead_confidence": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, P]),
         "dllm_qgemm_partials_i32": (I, [I, P, I64, I64, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -179,6 +180,35 @@ def lmhead_masked(qtype: int, w: torch.Tensor, N: int, K: int, h: torch.Tensor,
                                   _ptr(logits), logits.stride(0), _ptr(argmax), _ptr(workspace),
                                   wsb, _stream(dev)))
     return logits, argmax
+
+
+def lmhead_confidence(qtype: int, w: torch.Tensor, N: int, K: int, h: torch.Tensor,
+                      rows: torch.Tensor, logits: torch.Tensor | None = None,
+                      argmax: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      p_argmax: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """lmhead_masked plus the greedy pick's confidence: (f32 logits [n_rows,
+    N], int32 argmax [n_rows], f32 log-sum-exp [n_rows], f32 softmax
+    probability of the argmax [n_rows])."""
+    dev = _dev(w)
+    assert h.dtype == torch.float32 and h.stride(1) == 1 and rows.dtype == torch.int32
+    M = h.shape[0]
+    n = rows.numel()
+    if logits is None:
+        logits = torch.empty((n, N), dtype=torch.float32, device=dev)
+    if argmax is None:
+        argmax = torch.empty(n, dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+    if p_argmax is None:
+        p_argmax = torch.empty(n, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(lmhead_workspace_bytes(qtype, N, K, n), 1),
+                                dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib.dllm_lmhead_confidence(qtype, _ptr(w), N, K, _ptr(h), M, h.stride(0), _ptr(rows), n,
+                                      _ptr(logits), logits.stride(0), _ptr(argmax), _ptr(lse),
+                                      _ptr(p_argmax), _ptr(workspace), wsb, _stream(dev)))
+    return logits, argmax, lse, p_argmax
 
 
 def qgemm_partials_i32(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor,

@@ -292,6 +292,7 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
   p.xq = (const uint8_t*)x_q8k;
   p.dmax = x_dmax;
   p.keys = nullptr;
+  p.stats = nullptr;
   p.N = N;
   p.SB = K / 256;
   p.M = M;
@@ -316,10 +317,16 @@ static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Key slots per gathered row: one per 64-row tile (tiled path) or one per
 // wave (streaming path), whichever is more.
+static int64_t lmhead_slots(int64_t N) {
+  return cdiv(N, 64) > lmhead_stream_waves() ? cdiv(N, 64) : lmhead_stream_waves();
+}
+
+// Workspace: the gathered Q8_K rows, then per slot and row an argmax key (u64)
+// and softmax statistics (two f32).
 int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_rows) {
   if (check_qtype(qtype) || N <= 0 || K <= 0 || K % 256 || n_rows <= 0) return -1;
-  const int64_t slots = cdiv(N, 64) > lmhead_stream_waves() ? cdiv(N, 64) : lmhead_stream_waves();
-  return align256(n_rows * (K / 256) * Q8K_BYTES) + slots * n_rows * 8;
+  return align256(n_rows * (K / 256) * Q8K_BYTES) + align256(lmhead_slots(N) * n_rows * 8) +
+         lmhead_slots(N) * n_rows * 8;
 }
 
 // DLLM_LMHEAD_TILED=1 selects the tiled GEMM path even where the streaming
@@ -329,38 +336,44 @@ static bool lmhead_force_tiled() {
   return e && e[0] == '1' && !e[1];
 }
 
-int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
-                       const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax,
-                       void* workspace, int64_t workspace_bytes, void* stream) {
+// dllm_lmhead_masked, and with lse / p_max (both or neither) dllm_lmhead_confidence.
+static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M,
+                       int64_t ldh, const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl,
+                       int32_t* argmax, float* lse, float* p_max, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
   int rc = check_qtype(qtype);
   if (rc) return rc;
   if (!w || !h || !rows || !logits || !argmax || !workspace)
     return fail(DLLM_E_ARG,
-                "dllm_lmhead_masked: null pointer (w=%p, h=%p, rows=%p, logits=%p, argmax=%p, workspace=%p)", w,
+                "%s: null pointer (w=%p, h=%p, rows=%p, logits=%p, argmax=%p, workspace=%p)", fn, w,
                 (const void*)h, (const void*)rows, (void*)logits, (void*)argmax, workspace);
   if (N <= 0 || M <= 0 || K <= 0 || K % 256)
-    return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: need N > 0, M > 0, K a positive multiple of 256 (N=%lld, K=%lld, M=%lld)",
+    return fail(DLLM_E_SHAPE, "%s: need N > 0, M > 0, K a positive multiple of 256 (N=%lld, K=%lld, M=%lld)", fn,
                 (long long)N, (long long)K, (long long)M);
   if (n_rows < 1 || n_rows > M)
-    return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: n_rows=%lld must be in [1, M=%lld]", (long long)n_rows, (long long)M);
-  if (N > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "dllm_lmhead_masked: N=%lld exceeds 2^31-1", (long long)N);
-  if ((rc = check_buffer_sizes("dllm_lmhead_masked", qtype, N, K, n_rows))) return rc;
-  if (ldh < K) return fail(DLLM_E_ARG, "dllm_lmhead_masked: ldh=%lld < K=%lld", (long long)ldh, (long long)K);
-  if (ldl < N) return fail(DLLM_E_ARG, "dllm_lmhead_masked: ldl=%lld < N=%lld", (long long)ldl, (long long)N);
+    return fail(DLLM_E_SHAPE, "%s: n_rows=%lld must be in [1, M=%lld]", fn, (long long)n_rows, (long long)M);
+  if (N > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "%s: N=%lld exceeds 2^31-1", fn, (long long)N);
+  if ((rc = check_buffer_sizes(fn, qtype, N, K, n_rows))) return rc;
+  if (ldh < K) return fail(DLLM_E_ARG, "%s: ldh=%lld < K=%lld", fn, (long long)ldh, (long long)K);
+  if (ldl < N) return fail(DLLM_E_ARG, "%s: ldl=%lld < N=%lld", fn, (long long)ldl, (long long)N);
   if ((rc = check_weights(qtype, w))) return rc;
   if (!aligned(h, 4) || !aligned(logits, 4) || !aligned(rows, 4) || !aligned(argmax, 4))
-    return fail(DLLM_E_ALIGN, "dllm_lmhead_masked: h, rows, logits and argmax must be 4-byte aligned");
-  if (!aligned(workspace, 256)) return fail(DLLM_E_ALIGN, "dllm_lmhead_masked: workspace must be 256-byte aligned");
+    return fail(DLLM_E_ALIGN, "%s: h, rows, logits and argmax must be 4-byte aligned", fn);
+  if (!aligned(workspace, 256)) return fail(DLLM_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if ((lse == nullptr) != (p_max == nullptr))
+    return fail(DLLM_E_ARG, "%s: lse and p_argmax are both given or both null (lse=%p, p_argmax=%p)", fn, (void*)lse,
+                (void*)p_max);
+  if (!aligned(lse, 4) || !aligned(p_max, 4)) return fail(DLLM_E_ALIGN, "%s: lse and p_argmax must be 4-byte aligned", fn);
   const int64_t need = dllm_lmhead_workspace_bytes(qtype, N, K, n_rows);
   if (workspace_bytes < need)
-    return fail(DLLM_E_WORKSPACE, "dllm_lmhead_masked: workspace of %lld bytes, need %lld", (long long)workspace_bytes,
+    return fail(DLLM_E_WORKSPACE, "%s: workspace of %lld bytes, need %lld", fn, (long long)workspace_bytes,
                 (long long)need);
   hipStream_t s = (hipStream_t)stream;
   const int64_t SB = K / 256;
   uint8_t* xq = (uint8_t*)workspace;
   uint64_t* keys = (uint64_t*)((uint8_t*)workspace + align256(n_rows * SB * Q8K_BYTES));
-  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, nullptr, s),
-                       "dllm_lmhead_masked gather/quantize launch")))
+  float2* stats = lse ? (float2*)((uint8_t*)keys + align256(lmhead_slots(N) * n_rows * 8)) : nullptr;
+  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, nullptr, s), "lm head gather/quantize launch")))
     return rc;
   if (lmhead_stream_fits(K, n_rows) && !lmhead_force_tiled()) {
     LmParams lp;
@@ -368,13 +381,14 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
     lp.xq = xq;
     lp.logits = logits;
     lp.keys = keys;
+    lp.stats = stats;
     lp.N = N;
     lp.SB = SB;
     lp.M = n_rows;
     lp.ldl = ldl;
-    if ((rc = hip_status(launch_lmhead_stream(qtype, lp, s), "dllm_lmhead_masked stream launch"))) return rc;
-    return hip_status(launch_argmax_finalize(keys, lmhead_stream_slots(N), n_rows, argmax, s),
-                      "dllm_lmhead_masked argmax launch");
+    if ((rc = hip_status(launch_lmhead_stream(qtype, lp, s), "lm head stream launch"))) return rc;
+    return hip_status(launch_argmax_finalize(keys, stats, lmhead_stream_slots(N), n_rows, argmax, lse, p_max, s),
+                      "lm head argmax launch");
   }
   GemmParams p;
   p.w = (const uint8_t*)w;
@@ -382,6 +396,7 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   p.dmax = nullptr;
   p.out = logits;
   p.keys = keys;
+  p.stats = stats;
   p.N = N;
   p.SB = SB;
   p.M = n_rows;
@@ -391,8 +406,24 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
   const int tb = tb_for(n_rows);
   const int64_t n_tiles = cdiv(N, 64);  // 4 waves, 64 rows per work-group
   const dim3 grid((unsigned)n_tiles, 1, (unsigned)cdiv(n_rows, 16 * tb));
-  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 1, grid, true, s), "dllm_lmhead_masked gemm launch"))) return rc;
-  return hip_status(launch_argmax_finalize(keys, n_tiles, n_rows, argmax, s), "dllm_lmhead_masked argmax launch");
+  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 1, grid, true, s), "lm head gemm launch"))) return rc;
+  return hip_status(launch_argmax_finalize(keys, stats, n_tiles, n_rows, argmax, lse, p_max, s), "lm head argmax launch");
+}
+
+int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
+                       const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  return lmhead_impl("dllm_lmhead_masked", qtype, w, N, K, h, M, ldh, rows, n_rows, logits, ldl, argmax, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int dllm_lmhead_confidence(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
+                           const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax,
+                           float* lse, float* p_argmax, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!lse || !p_argmax)
+    return fail(DLLM_E_ARG, "dllm_lmhead_confidence: null pointer (lse=%p, p_argmax=%p)", (void*)lse, (void*)p_argmax);
+  return lmhead_impl("dllm_lmhead_confidence", qtype, w, N, K, h, M, ldh, rows, n_rows, logits, ldl, argmax, lse,
+                     p_argmax, workspace, workspace_bytes, stream);
 }
 
 int dllm_qgemm_partials_i32(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M, int32_t* P,

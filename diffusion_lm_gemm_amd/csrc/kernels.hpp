@@ -12,6 +12,7 @@ struct GemmParams {
   const float* dmax;     // per token, the largest |d| of its blocks, or null
   float* out;            // y (no split) or split partials
   uint64_t* keys;        // argmax keys [n_tiles][M] (LM head) or null
+  float2* stats;         // with keys: softmax statistics (m, s) [n_tiles][M], or null
   int64_t N, SB, M;
   int64_t ldo;           // leading dimension of out
   int64_t split_stride;  // floats between split slices of out
@@ -25,6 +26,7 @@ struct LmParams {
   const uint8_t* xq;
   float* logits;
   uint64_t* keys;
+  float2* stats;  // softmax statistics (m, s) [wave][M], or null
   int64_t N, SB, M;
   int64_t ldl;
 };
@@ -46,7 +48,10 @@ bool lmhead_stream_fits(int64_t K, int64_t n_rows);
 int lmhead_stream_waves();             // the most waves (key slots per row) it uses
 int64_t lmhead_stream_slots(int64_t N);  // the waves it uses for N rows
 hipError_t launch_lmhead_stream(int qtype, const LmParams& p, hipStream_t s);
-hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s);
+// stats != nullptr: also lse[m] = log-sum-exp and p_max[m] = softmax probability
+// of the argmax, from the per-tile (m, s) statistics.
+hipError_t launch_argmax_finalize(const uint64_t* keys, const float2* stats, int64_t n_tiles, int64_t M,
+                                  int32_t* argmax, float* lse, float* p_max, hipStream_t s);
 hipError_t launch_partials(int qtype, const uint8_t* w, int64_t N, int64_t SB, const uint8_t* xq, int64_t M,
                            int32_t* P, hipStream_t s);
 

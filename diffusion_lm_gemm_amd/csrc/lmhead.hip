@@ -113,6 +113,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
 
   v4f yacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   uint64_t best[2] = {0, 0};
+  // softmax statistics (m, s) per token over the lane's rows (when asked for)
+  const bool want_stats = p.stats != nullptr;
+  float sm[2] = {-__builtin_inff(), -__builtin_inff()}, ss[2] = {0.0f, 0.0f};
   uint32_t mh0 = 0, mh2 = 0, mh3 = 0;
   int64_t k = 0;   // row block index of this wave's stream
   int sb = 0;      // super-block within it
@@ -207,6 +210,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
           const uint64_t key = ((uint64_t)f32_order_bits(yv[i]) << 32) | (uint64_t)(~(uint32_t)(nbase + i));
           best[t] = (nbase + i < N && key > best[t]) ? key : best[t];
         }
+        if (want_stats) {
+          const float l[4] = {yv[0], yv[1], yv[2], yv[3]};
+          const bool ok[4] = {nbase < N, nbase + 1 < N, nbase + 2 < N, nbase + 3 < N};
+          softmax_add4(sm[t], ss[t], l, ok);
+        }
         yacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -241,6 +249,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
     b = o2 > b ? o2 : b;
     const int64_t m = t * 16 + r;
     if (g4 == 0 && m < M) p.keys[wave * M + m] = b;
+    if (want_stats) {
+      softmax_merge_groups(sm[t], ss[t]);
+      if (g4 == 0 && m < M) p.stats[wave * M + m] = float2{sm[t], ss[t]};
+    }
   }
 }
 

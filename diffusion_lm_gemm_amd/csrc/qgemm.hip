@@ -93,6 +93,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   __shared__ float s_esc[TOK];
   __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTHL - NITEM) + 8 : 8];
   __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
+  __shared__ float2 s_stat[ARGMAX ? NW * TOK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -587,6 +588,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       const uint64_t o2 = __shfl_xor(best, 32);
       best = o2 > best ? o2 : best;
       if (g4 == 0) s_key[wv * TOK + t * 16 + r] = best;
+      if (p.stats) {
+        // softmax statistics of this token over the wave's rows
+        float sm = -__builtin_inff(), ss = 0.0f;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const float l[4] = {yacc[b][t][0], yacc[b][t][1], yacc[b][t][2], yacc[b][t][3]};
+          bool ok[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ok[i] = row0 + 16 * b + 4 * g4 + i < N;
+          softmax_add4(sm, ss, l, ok);
+        }
+        softmax_merge_groups(sm, ss);
+        if (g4 == 0) s_stat[wv * TOK + t * 16 + r] = float2{sm, ss};
+      }
     }
     __syncthreads();
     if (tid < TOK) {
@@ -595,6 +610,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
       for (int k = 1; k < NW; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
       if (m < M) p.keys[(int64_t)blockIdx.x * M + m] = best;
+      if (p.stats) {
+        float sm = s_stat[tid].x, ss = s_stat[tid].y;
+#pragma unroll
+        for (int k = 1; k < NW; ++k) softmax_merge(sm, ss, s_stat[k * TOK + tid].x, s_stat[k * TOK + tid].y);
+        if (m < M) p.stats[(int64_t)blockIdx.x * M + m] = float2{sm, ss};
+      }
     }
   }
 }
@@ -655,22 +676,46 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
 }
 
 // argmax[m] = lowest row index of the largest logit, from per-tile keys.
-__global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restrict__ keys, int64_t n_tiles,
-                                                       int64_t M, int32_t* __restrict__ argmax) {
+// With stats, also the row's log-sum-exp and the softmax probability of its
+// largest logit, from the per-tile (m, s) statistics merged in a tree.
+__global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restrict__ keys,
+                                                       const float2* __restrict__ stats, int64_t n_tiles,
+                                                       int64_t M, int32_t* __restrict__ argmax,
+                                                       float* __restrict__ lse, float* __restrict__ p_max) {
   __shared__ uint64_t red[256];
+  __shared__ float2 sred[256];
   const int64_t m = blockIdx.x;
   uint64_t best = 0;
+  float sm = -__builtin_inff(), ss = 0.0f;
   for (int64_t t = threadIdx.x; t < n_tiles; t += 256) {
     const uint64_t k = keys[t * M + m];
     best = k > best ? k : best;
+    if (stats) {
+      const float2 st = stats[t * M + m];
+      softmax_merge(sm, ss, st.x, st.y);
+    }
   }
   red[threadIdx.x] = best;
+  sred[threadIdx.x] = float2{sm, ss};
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s && red[threadIdx.x + s] > red[threadIdx.x]) red[threadIdx.x] = red[threadIdx.x + s];
+    if ((int)threadIdx.x < s) {
+      if (red[threadIdx.x + s] > red[threadIdx.x]) red[threadIdx.x] = red[threadIdx.x + s];
+      if (stats) {
+        float a = sred[threadIdx.x].x, b = sred[threadIdx.x].y;
+        softmax_merge(a, b, sred[threadIdx.x + s].x, sred[threadIdx.x + s].y);
+        sred[threadIdx.x] = float2{a, b};
+      }
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) argmax[m] = (int32_t)(~(uint32_t)(red[0] & 0xFFFFFFFFu));
+  if (threadIdx.x == 0) {
+    argmax[m] = (int32_t)(~(uint32_t)(red[0] & 0xFFFFFFFFu));
+    if (stats) {
+      lse[m] = sred[0].x + logf(sred[0].y);
+      p_max[m] = 1.0f / sred[0].y;
+    }
+  }
 }
 
 // Test export: per-16 integer partial dots of the unsigned shared-form quants
@@ -798,8 +843,10 @@ hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, flo
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_finalize(const uint64_t* keys, int64_t n_tiles, int64_t M, int32_t* argmax, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_finalize, dim3((unsigned)M), dim3(256), 0, s, keys, n_tiles, M, argmax);
+hipError_t launch_argmax_finalize(const uint64_t* keys, const float2* stats, int64_t n_tiles, int64_t M,
+                                  int32_t* argmax, float* lse, float* p_max, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3((unsigned)M), dim3(256), 0, s, keys, stats, n_tiles, M, argmax, lse,
+                     p_max);
   return hipGetLastError();
 }
 

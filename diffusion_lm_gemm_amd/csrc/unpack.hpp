@@ -255,4 +255,32 @@ __device__ __forceinline__ uint32_t f32_order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Softmax statistics of a set of logits as (m, s): m its largest logit and
+// s = sum exp(l - m) (m = -inf, s = 0 for the empty set).  Two sets merge by
+// rescaling both sums to the larger maximum, so the per-row statistics can be
+// gathered over waves and work-groups in any grouping; the log-sum-exp is
+// m + log s and the softmax probability of the largest logit 1 / s.
+__device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -__builtin_inff()) return;  // both empty
+  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  m = mn;
+}
+// four logits of which those with ok[i] belong to the set
+__device__ __forceinline__ void softmax_add4(float& m, float& s, const float (&l)[4], const bool (&ok)[4]) {
+  float m4 = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m4 = ok[i] ? fmaxf(m4, l[i]) : m4;
+  if (m4 == -__builtin_inff()) return;
+  float s4 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4 += ok[i] ? expf(l[i] - m4) : 0.0f;
+  softmax_merge(m, s, m4, s4);
+}
+// merge over the four 16-lane groups of a wave (lanes r, r + 16, r + 32, r + 48)
+__device__ __forceinline__ void softmax_merge_groups(float& m, float& s) {
+  softmax_merge(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16));
+  softmax_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
+}
+
 }  // namespace dllm

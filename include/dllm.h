@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 2
+#define DLLM_ABI_VERSION 3
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -123,7 +123,10 @@ int dllm_qgemm(int qtype, const void *w, int64_t N, int64_t K,
  *   logits  f32 [n_rows][ldl], ldl >= N (written)
  *   argmax  int32 [n_rows] (written)
  *   workspace  at least dllm_lmhead_workspace_bytes(qtype, N, K, n_rows) bytes,
- *           256-byte aligned (required)
+ *           256-byte aligned (required); its contents on entry do not matter
+ *           (the call writes the gathered Q8_K rows and per-wave or per-tile
+ *           argmax keys there), and calls sharing one workspace must be
+ *           ordered on one stream
  * n_rows may be 1..M; the kernels are tuned for n_rows <= 32 (LLaDA's block).
  */
 int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_rows);
@@ -132,6 +135,27 @@ int dllm_lmhead_masked(int qtype, const void *w, int64_t N, int64_t K,
                        const int32_t *rows, int64_t n_rows, float *logits,
                        int64_t ldl, int32_t *argmax, void *workspace,
                        int64_t workspace_bytes, void *stream);
+
+/*
+ * The masked-row LM head plus the confidence of the greedy pick (README
+ * "How it works", "Each model's own sampler": LLaDA's low-confidence
+ * remasking ranks masked positions by the softmax probability of the token
+ * it would commit; Development plan, "Sampling", lists softmax, log-softmax
+ * and argmax).  Everything dllm_lmhead_masked writes, and per gathered row
+ *   lse       f32 [n_rows]: log(sum_n exp(logits[r][n])) over the row's N
+ *             logits as written (natural log)
+ *   p_argmax  f32 [n_rows]: softmax probability of argmax[r], i.e.
+ *             exp(logits[r][argmax[r]] - lse[r])
+ * Both are device pointers, 4-byte aligned, required.  They are computed in
+ * f32 from per-wave (or per-tile) running maxima and rescaled exponential
+ * sums, merged in the argmax kernel; the same workspace size applies.
+ */
+int dllm_lmhead_confidence(int qtype, const void *w, int64_t N, int64_t K,
+                           const float *h, int64_t M, int64_t ldh,
+                           const int32_t *rows, int64_t n_rows, float *logits,
+                           int64_t ldl, int32_t *argmax, float *lse,
+                           float *p_argmax, void *workspace,
+                           int64_t workspace_bytes, void *stream);
 
 /*
  * Test export: per-16 integer partial dots of the shared form,

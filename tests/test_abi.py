@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -102,6 +102,26 @@ def test_lmhead_argument_errors(dl):
     assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 256, FAKE, 4, FAKE, 1000, FAKE, ws, ok_ws, None) == dl.E_ARG
     assert L.dllm_lmhead_masked(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
                                 ctypes.c_void_p((1 << 24) + 16), ok_ws, None) == dl.E_ALIGN
+
+
+def test_lmhead_confidence_argument_errors(dl):
+    L = dl.lib
+    ok_ws = dl.lmhead_workspace_bytes(dl.Q6_K, 1000, 512, 4)
+    ws = ctypes.c_void_p(1 << 24)
+    # lse and p_argmax are required, and 4-byte aligned
+    assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                    None, FAKE, ws, ok_ws, None) == dl.E_ARG
+    assert "lse" in dl.last_error()
+    assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                    FAKE, None, ws, ok_ws, None) == dl.E_ARG
+    assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                    ctypes.c_void_p((1 << 20) + 2), FAKE, ws, ok_ws, None) == dl.E_ALIGN
+    # the shared checks name this entry point
+    assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 3, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                    FAKE, FAKE, ws, ok_ws, None) == dl.E_SHAPE
+    assert "dllm_lmhead_confidence" in dl.last_error()
+    assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
+                                    FAKE, FAKE, ws, ok_ws - 1, None) == dl.E_WORKSPACE
 
 
 def test_workspace_queries(dl):

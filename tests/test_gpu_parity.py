@@ -461,6 +461,51 @@ def test_lmhead_exact_tie_picks_lowest_index(dl, K):
     assert am[0] == 77
 
 
+def _check_confidence(logits, lse, p, ref_logits, what):
+    """lse and p(argmax) against (1) the f64 statistics of the GPU's own f32
+    logits, which isolates the f32 reduction (exp/log rounding and the merge
+    order: a few ulp per term), and (2) the oracle's, within what the logit
+    bound allows: the log-sum-exp moves by at most the largest logit error
+    e = max_n 1e-4 (|l_n| + rms), and log p = max - lse by at most 2e."""
+    own_lse, own_p = oracle.softmax_stats(logits.astype(np.float64))
+    assert np.all(np.abs(lse - own_lse) <= 4e-6 * (1.0 + np.abs(own_lse))), f"{what}: lse vs own logits"
+    assert np.all(np.abs(p / own_p - 1.0) <= 4e-6 * (1.0 + np.abs(own_lse))), f"{what}: p vs own logits"
+    ref_lse, ref_p = oracle.softmax_stats(ref_logits)
+    rms = np.sqrt(np.mean(ref_logits ** 2, axis=1))
+    e = 1e-4 * (np.abs(ref_logits).max(axis=1) + rms)
+    assert np.all(np.abs(lse - ref_lse) <= e + 4e-6 * (1.0 + np.abs(ref_lse))), f"{what}: lse vs oracle"
+    assert np.all(np.abs(np.log(p) - np.log(ref_p)) <= 2 * e + 4e-6 * (1.0 + np.abs(ref_lse))), f"{what}: p vs oracle"
+    _say(f"{what}: lse {lse[:3]} p(argmax) {p[:3]}")
+
+
+@pytest.mark.parametrize("qtype", [12, 14])
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("scale", [1.0, 0.002])
+def test_lmhead_confidence(dl, monkeypatch, qtype, tiled, scale):
+    """dllm_lmhead_confidence on both LM-head paths: the same logits and
+    argmax as dllm_lmhead_masked, plus the log-sum-exp and the softmax
+    probability of the argmax, for peaked (scale 1) and flat (scale 0.002)
+    logit rows over a ragged 1000-row vocabulary."""
+    if tiled:
+        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
+    N, K, M = 1000, 2048, 148
+    _say(f"lmhead confidence qtype={qtype} tiled={tiled} scale={scale}")
+    w = _weights(qtype, N, K, 21, f"conf-{qtype}")
+    h = synth.normal_f32((M, K), 21, "conf-h") * scale
+    rows = synth.distinct_rows(13, M, 21, "conf-rows")
+    ref, ref_am = oracle.lmhead(qtype, w.numpy(), N, K, h.numpy(), rows.numpy())
+    wd, hd, rd = w.to(DEV), h.to(DEV), rows.to(DEV)
+    logits, am, lse, p = dl.lmhead_confidence(qtype, wd, N, K, hd, rd)
+    logits2, am2 = dl.lmhead_masked(qtype, wd, N, K, hd, rd)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, logits2) and torch.equal(am, am2)
+    lg = logits.cpu().numpy()
+    assert_close_rows(lg, ref, f"confidence logits qtype={qtype} tiled={tiled}")
+    _check_argmax(lg, am.cpu().numpy(), ref, ref_am, "confidence argmax")
+    _check_confidence(lg, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
+                      f"confidence qtype={qtype} tiled={tiled} scale={scale}")
+
+
 def test_lmhead_full_size(dl):
     """Masked-row LM head: 32 masked canvas rows (20..51 of 148) x LLaDA's
     untied 126464 x 4096 output matrix in Q6_K, against the full oracle."""
@@ -474,3 +519,9 @@ def test_lmhead_full_size(dl):
     logits = logits.cpu().numpy(); am = am.cpu().numpy()
     assert_close_rows(logits, ref, "lmhead full")
     _check_argmax(logits, am, ref, ref_am, "lmhead full")
+    # the confidence entry point on the same inputs: same logits, and the
+    # statistics over all 126464 logits of each row
+    lg2, am2, lse, p = dl.lmhead_confidence(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    assert np.array_equal(lg2.cpu().numpy(), logits) and np.array_equal(am2.cpu().numpy(), am)
+    _check_confidence(logits, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
+                      "lmhead full confidence")
