@@ -59,6 +59,8 @@ def lib():
         for name, args in {
             "oracle_decode_rows": [I, P, I64, I64, P],
             "oracle_softmax_stats": [P, I64, I64, P, P],
+            "oracle_rmsnorm_quantize_q8k": [P, I64, I64, I64, P, ctypes.c_float, P, P],
+            "oracle_swiglu_quantize_q8k": [P, I64, I64, I64, P, P],
             "oracle_decode_shared": [I, P, I64, P],
             "oracle_quantize_q8k": [P, I64, I64, I64, P],
             "oracle_dequant_q8k": [P, I64, I64, P],
@@ -200,3 +202,30 @@ def softmax_stats(logits: np.ndarray):
     p = np.zeros(n, np.float64)
     _check(lib().oracle_softmax_stats(_p(lg), n, N, _p(lse), _p(p)), "softmax_stats")
     return lse, p
+
+
+def rmsnorm_quantize_q8k(x: np.ndarray, g: np.ndarray, eps: float):
+    """(Q8_K records uint8 [M, K/256*292], f32 dmax [M]) of RMSNorm(x) with
+    norm weight g: the codes of f32(x*g), each block's d times the row's
+    f32 factor 1/sqrt(mean(x^2) + eps)."""
+    x = np.ascontiguousarray(x, np.float32)
+    g = np.ascontiguousarray(g, np.float32)
+    M, K = x.shape
+    out = np.zeros((M, K // 256 * 292), np.uint8)
+    dmax = np.zeros(M, np.float32)
+    _check(lib().oracle_rmsnorm_quantize_q8k(_p(x), M, K, K, _p(g), float(eps), _p(out), _p(dmax)),
+           "rmsnorm_quantize_q8k")
+    return out, dmax
+
+
+def swiglu_quantize_q8k(gu: np.ndarray):
+    """(Q8_K records uint8 [M, F/256*292], f32 dmax [M]) of silu(gate) * up,
+    gate = gu[:, :F], up = gu[:, F:], evaluated in f64 and rounded once to
+    f32 before quantizing."""
+    gu = np.ascontiguousarray(gu, np.float32)
+    M, F2 = gu.shape
+    F = F2 // 2
+    out = np.zeros((M, F // 256 * 292), np.uint8)
+    dmax = np.zeros(M, np.float32)
+    _check(lib().oracle_swiglu_quantize_q8k(_p(gu), M, F, F2, _p(out), _p(dmax)), "swiglu_quantize_q8k")
+    return out, dmax

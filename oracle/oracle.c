@@ -421,3 +421,67 @@ int oracle_softmax_stats(const double *logits, int64_t n_rows, int64_t N, double
   }
   return 0;
 }
+
+/* ---- fused producers of the quantized activations ---------------------- */
+/* The pages' layer runs RMSNorm before the QKV and MLP projections (eps 1e-5
+ * for LLaDA) and a SwiGLU MLP, and list fused normalization among the next
+ * goals.  These are the two producers fused with the Q8_K quantizer.
+ *
+ * RMSNorm -> Q8_K, per row of x (K values) with norm weight g[K]:
+ *   r = f32(1 / sqrt(sum_k x_k^2 / K + eps))   (squares exact in f64, the sum
+ *                                              in f64 ascending, sqrt and
+ *                                              division in f64, one rounding)
+ *   z_k = f32(x_k * g_k)
+ *   the Q8_K blocks of z (codes and bsums), with each block's d replaced by
+ *   f32(r * d_z): the blocks of RMSNorm(x) = r * z with the common factor r
+ *   moved into the block scale, so the codes do not depend on r.
+ * dmax[m] (optional): the row's largest |d|. */
+int oracle_rmsnorm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx, const float *g, float eps,
+                                uint8_t *out, float *dmax) {
+  if (K % 256 || ldx < K) return -1;
+  const int64_t nsb = K / 256;
+  float *z = (float *)malloc(sizeof(float) * (size_t)K);
+  for (int64_t m = 0; m < M; ++m) {
+    const float *xr = x + m * ldx;
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) ss += (double)xr[k] * (double)xr[k];
+    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    for (int64_t k = 0; k < K; ++k) z[k] = xr[k] * g[k];
+    float mx = 0.0f;
+    for (int64_t s = 0; s < nsb; ++s) {
+      uint8_t *b = out + (m * nsb + s) * 292;
+      quantize_block_q8k(z + s * 256, b);
+      const float d = r * rdf32(b);
+      memcpy(b, &d, 4);
+      if (fabsf(d) > mx) mx = fabsf(d);
+    }
+    if (dmax) dmax[m] = mx;
+  }
+  free(z);
+  return 0;
+}
+
+/* SwiGLU -> Q8_K, per row of gu: gate = gu[0..F), up = gu[F..2F),
+ *   act_k = f32(gate_k * up_k / (1 + exp(-gate_k)))   (f64, one rounding)
+ * (silu(gate) * up), then the Q8_K blocks of act.  dmax as above. */
+int oracle_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F, int64_t ldgu, uint8_t *out, float *dmax) {
+  if (F % 256 || ldgu < 2 * F) return -1;
+  const int64_t nsb = F / 256;
+  float *a = (float *)malloc(sizeof(float) * (size_t)F);
+  for (int64_t m = 0; m < M; ++m) {
+    const float *gate = gu + m * ldgu, *up = gate + F;
+    for (int64_t k = 0; k < F; ++k) {
+      const double gd = (double)gate[k];
+      a[k] = (float)(gd * (double)up[k] / (1.0 + exp(-gd)));
+    }
+    float mx = 0.0f;
+    for (int64_t s = 0; s < nsb; ++s) {
+      uint8_t *b = out + (m * nsb + s) * 292;
+      quantize_block_q8k(a + s * 256, b);
+      if (fabsf(rdf32(b)) > mx) mx = fabsf(rdf32(b));
+    }
+    if (dmax) dmax[m] = mx;
+  }
+  free(a);
+  return 0;
+}

@@ -28,4 +28,8 @@ int oracle_lmhead(int qtype, const uint8_t *w, int64_t N, int64_t K,
                   int64_t n_rows, double *logits, int32_t *argmax, int nthreads);
 int oracle_softmax_stats(const double *logits, int64_t n_rows, int64_t N,
                          double *lse, double *p_argmax);
+int oracle_rmsnorm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
+                                const float *g, float eps, uint8_t *out, float *dmax);
+int oracle_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F, int64_t ldgu,
+                               uint8_t *out, float *dmax);
 #endif
