@@ -259,6 +259,46 @@ def main():
         b.record()
     torch.cuda.synchronize()
     conf_ms = sum(a.elapsed_time(b) for a, b in cev) / reps
+
+    # the fused producers of the quantized activations (not part of the step):
+    # RMSNorm -> Q8_K on a layer input, SwiGLU -> Q8_K on the gate/up output,
+    # against the plain quantizer on the f32 tensors they replace
+    g_norm = synth.normal_f32((D,), seed, "norm_weight", dev)
+    fused = {
+        "rmsnorm_quantize_q8k": (lambda: dl.rmsnorm_quantize_q8k(layers[0]["x_norm"], g_norm, 1e-5, xq_d, dmax_d),
+                                 L * D * 4 + D * 4 + L * D // 256 * 292),
+        "quantize_q8k_after_rmsnorm": (lambda: dl.quantize_q8k(layers[0]["x_norm"], xq_d, dmax_d),
+                                       L * D * 4 + L * D // 256 * 292),
+        "swiglu_quantize_q8k": (lambda: dl.swiglu_quantize_q8k(y_gu, xq_f, dmax_f),
+                                L * 2 * FFN * 4 + L * FFN // 256 * 292),
+        "quantize_q8k_after_swiglu": (lambda: dl.quantize_q8k(layers[0]["act"], xq_f, dmax_f),
+                                      L * FFN * 4 + L * FFN // 256 * 292),
+    }
+    fused_out = {}
+    for name, (fn, byts) in fused.items():
+        # per call as a node of a replayed graph of 20 calls, like the step's
+        fn()
+        torch.cuda.synchronize()
+        fg = torch.cuda.CUDAGraph()
+        fs = torch.cuda.Stream()
+        fs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(fs):
+            with torch.cuda.graph(fg, stream=fs):
+                for _ in range(20):
+                    fn()
+        torch.cuda.current_stream().wait_stream(fs)
+        fg.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fg.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / 20)
+        fms = sorted(times)[2]
+        fused_out[name] = {"avg_ms": round(fms, 5), "GBps": round(byts / (fms * 1e-3) / 1e9, 1)}
     print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
     print(f"[bench] per-call shapes: " + json.dumps(shapes), file=sys.stderr, flush=True)
 
@@ -317,6 +357,7 @@ def main():
         "lmhead_confidence": {"avg_ms": round(conf_ms, 5), "GBps": round(lm_bytes / (conf_ms * 1e-3) / 1e9, 1),
                               "outputs": "logits, argmax, log-sum-exp and p(argmax) per masked row",
                               "in_step": False},
+        "fused_producers": dict(fused_out, in_step=False),
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),
     }

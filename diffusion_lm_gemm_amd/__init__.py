@@ -28,7 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdllm.so")
 
 HEADER_EXPORTS = (
-    "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_decode_qk",
+    "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_rmsnorm_quantize_q8k",
+    "dllm_swiglu_quantize_q8k", "dllm_decode_qk",
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
 )
@@ -50,6 +51,8 @@ def _load():
         "dllm_abi_version": (I, []),
         "dllm_last_error": (ctypes.c_char_p, []),
         "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
+        "dllm_rmsnorm_quantize_q8k": (I, [P, I64, I64, I64, P, ctypes.c_float, P, P, P]),
+        "dllm_swiglu_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
         "dllm_decode_qk": (I, [I, P, I64, P, P]),
         "dllm_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_qgemm": (I, [I, P, I64, I64, P, P, I64, P, I64, P, I64, P]),
@@ -112,6 +115,41 @@ def quantize_q8k(x: torch.Tensor, out: torch.Tensor | None = None,
     if dmax is not None:
         assert dmax.dtype == torch.float32 and dmax.is_contiguous() and dmax.numel() >= M
     _check(lib.dllm_quantize_q8k(_ptr(x), M, K, x.stride(0), _ptr(out), _ptr(dmax), _stream(dev)))
+    return out
+
+
+def rmsnorm_quantize_q8k(x: torch.Tensor, g: torch.Tensor, eps: float = 1e-5,
+                         out: torch.Tensor | None = None,
+                         dmax: torch.Tensor | None = None) -> torch.Tensor:
+    """RMSNorm(x) * g -> Q8_K records uint8 [M, K/256*292] without the f32
+    intermediate: the codes of x * g, each block's d times the row's factor
+    1/sqrt(mean(x^2) + eps)."""
+    dev = _dev(x)
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    assert g.dtype == torch.float32 and g.is_contiguous()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K // QK_K * Q8_K_BYTES), dtype=torch.uint8, device=dev)
+    if dmax is not None:
+        assert dmax.dtype == torch.float32 and dmax.is_contiguous() and dmax.numel() >= M
+    _check(lib.dllm_rmsnorm_quantize_q8k(_ptr(x), M, K, x.stride(0), _ptr(g), float(eps), _ptr(out), _ptr(dmax),
+                                         _stream(dev)))
+    return out
+
+
+def swiglu_quantize_q8k(gu: torch.Tensor, out: torch.Tensor | None = None,
+                        dmax: torch.Tensor | None = None) -> torch.Tensor:
+    """f32 [M, 2F] (gate | up) -> the Q8_K records [M, F/256*292] of
+    silu(gate) * up, evaluated in f64 and rounded once to f32."""
+    dev = _dev(gu)
+    assert gu.dtype == torch.float32 and gu.dim() == 2 and gu.stride(1) == 1
+    M, F2 = gu.shape
+    F = F2 // 2
+    if out is None:
+        out = torch.empty((M, F // QK_K * Q8_K_BYTES), dtype=torch.uint8, device=dev)
+    if dmax is not None:
+        assert dmax.dtype == torch.float32 and dmax.is_contiguous() and dmax.numel() >= M
+    _check(lib.dllm_swiglu_quantize_q8k(_ptr(gu), M, F, gu.stride(0), _ptr(out), _ptr(dmax), _stream(dev)))
     return out
 
 

@@ -245,6 +245,41 @@ int dllm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, void* y
                     "dllm_quantize_q8k launch");
 }
 
+int dllm_rmsnorm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, const float* g, float eps,
+                              void* y_q8k, float* dmax, void* stream) {
+  const char* fn = "dllm_rmsnorm_quantize_q8k";
+  if (!x || !g || !y_q8k)
+    return fail(DLLM_E_ARG, "%s: null pointer (x=%p, g=%p, y=%p)", fn, (const void*)x, (const void*)g, y_q8k);
+  if (M <= 0 || K <= 0 || K % 256)
+    return fail(DLLM_E_SHAPE, "%s: need M > 0 and K a positive multiple of 256 (M=%lld, K=%lld)", fn, (long long)M,
+                (long long)K);
+  if (!rmsnorm_quantize_fits(K / 256))
+    return fail(DLLM_E_SHAPE, "%s: K=%lld exceeds 16384 (the fused normalization keeps a row's block scales in LDS)",
+                fn, (long long)K);
+  if (ldx < K) return fail(DLLM_E_ARG, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(DLLM_E_ARG, "%s: eps=%g must be in [0, 1]", fn, (double)eps);
+  if (!aligned(x, 4) || !aligned(g, 4) || !aligned(y_q8k, 4) || !aligned(dmax, 4))
+    return fail(DLLM_E_ALIGN, "%s: x, g, y and dmax must be 4-byte aligned", fn);
+  if (M > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "%s: M=%lld exceeds 2^31-1", fn, (long long)M);
+  return hip_status(launch_rmsnorm_quantize_q8k(x, ldx, M, K / 256, g, eps, (uint8_t*)y_q8k, dmax, (hipStream_t)stream),
+                    "dllm_rmsnorm_quantize_q8k launch");
+}
+
+int dllm_swiglu_quantize_q8k(const float* gu, int64_t M, int64_t F, int64_t ldgu, void* y_q8k, float* dmax,
+                             void* stream) {
+  const char* fn = "dllm_swiglu_quantize_q8k";
+  if (!gu || !y_q8k) return fail(DLLM_E_ARG, "%s: null pointer (gu=%p, y=%p)", fn, (const void*)gu, y_q8k);
+  if (M <= 0 || F <= 0 || F % 256)
+    return fail(DLLM_E_SHAPE, "%s: need M > 0 and F a positive multiple of 256 (M=%lld, F=%lld)", fn, (long long)M,
+                (long long)F);
+  if (ldgu < 2 * F) return fail(DLLM_E_ARG, "%s: ldgu=%lld < 2F=%lld", fn, (long long)ldgu, (long long)(2 * F));
+  if (!aligned(gu, 4) || !aligned(y_q8k, 4) || !aligned(dmax, 4))
+    return fail(DLLM_E_ALIGN, "%s: gu, y and dmax must be 4-byte aligned", fn);
+  if (M > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "%s: M=%lld exceeds 2^31-1", fn, (long long)M);
+  return hip_status(launch_swiglu_quantize_q8k(gu, ldgu, M, F / 256, (uint8_t*)y_q8k, dmax, (hipStream_t)stream),
+                    "dllm_swiglu_quantize_q8k launch");
+}
+
 int dllm_decode_qk(int qtype, const void* w, int64_t n_superblocks, void* out, void* stream) {
   int rc = check_qtype(qtype);
   if (rc) return rc;

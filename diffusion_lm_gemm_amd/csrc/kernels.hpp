@@ -33,6 +33,12 @@ struct LmParams {
 
 hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
                                float* dmax, hipStream_t s);
+// Fused producers (RMSNorm -> Q8_K with K <= 16384, SwiGLU -> Q8_K; see quantize.hip).
+bool rmsnorm_quantize_fits(int64_t SB);
+hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, int64_t SB, const float* g, float eps,
+                                       uint8_t* y, float* dmax, hipStream_t s);
+hipError_t launch_swiglu_quantize_q8k(const float* gu, int64_t ldgu, int64_t M, int64_t SB, uint8_t* y, float* dmax,
+                                      hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
 // cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
 // 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up

@@ -50,8 +50,10 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t v) {
 }
 
 // Quantize one 256-value block held as v[0..3] = values 4 lane .. 4 lane + 3
-// into the 292-byte record at `out` (written only if `store`); returns |d|.
-__device__ __forceinline__ float quantize_block(const float (&v)[4], uint8_t* out, int lane, bool store) {
+// into the 292-byte record at `out` (written only if `store`; its d only if
+// also `store_d`); returns d (0 if not `store`).
+__device__ __forceinline__ float quantize_block(const float (&v)[4], uint8_t* out, int lane, bool store,
+                                               bool store_d = true) {
 #pragma clang fp contract(off)
   float a[4];
   float lm = 0.0f;
@@ -88,76 +90,174 @@ __device__ __forceinline__ float quantize_block(const float (&v)[4], uint8_t* ou
   if (store) {
     ((uint32_t*)(out + 4))[lane] = packed;
     if ((lane & 3) == 0) ((int16_t*)(out + 260))[lane >> 2] = (int16_t)(int32_t)s;
-    if (lane == 0) *(float*)out = d;
+    if (lane == 0 && store_d) *(float*)out = d;
   }
-  return store ? __builtin_fabsf(d) : 0.0f;
+  return store ? d : 0.0f;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 }  // namespace
 
-// rows != nullptr gathers token m from row rows[m] of x (masked-row LM head);
-// dmax != nullptr receives each row's largest |d|.  QU = blocks per wave in
-// flight: a block index past the row loads the row's last block again and
-// stores nothing.
-template <int QU>
-__global__ __launch_bounds__(64 * QW) void k_quantize_q8k(const float* __restrict__ x, int64_t ldx,
-                                                     const int32_t* __restrict__ rows, int64_t SB,
-                                                     uint8_t* __restrict__ y, float* __restrict__ dmax) {
+// Modes of the quantizer: the block values are the row of x itself (PLAIN,
+// with an optional row gather for the LM head), or a producer fused in front
+// of it:
+//   RMSNORM: the codes of z = f32(x * g) (g the norm weight), each block's d
+//            times the row's r = f32(1 / sqrt(mean(x^2) + eps)), the sum of
+//            squares in f64: the blocks of RMSNorm(x) with the common factor r
+//            moved into the block scales;
+//   SWIGLU:  the row holds gate (values 0..K) and up (K..2K); the values are
+//            f32(gate * up / (1 + exp(-gate))), evaluated in f64.
+enum { Q_PLAIN = 0, Q_RMSNORM = 1, Q_SWIGLU = 2 };
+constexpr int RMS_SBMAX = 64;  // blocks per row in RMSNORM mode (K <= 16384)
+
+struct QuantArgs {
+  const float* x;
+  int64_t ldx;
+  const int32_t* rows;  // PLAIN: gather rows[m] (or null)
+  int64_t SB;           // blocks per output row
+  uint8_t* y;
+  float* dmax;          // per row, the largest |d| (or null)
+  const float* g;       // RMSNORM: norm weight [K]
+  float eps;            // RMSNORM
+};
+
+__device__ __forceinline__ void load4(const float* p, bool vec, float (&v)[4]) {
+  if (vec) {
+    const float4 t = *(const float4*)p;
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p[i];
+  }
+}
+
+// QU = blocks per wave in flight: a block index past the row loads the row's
+// last block again and stores nothing.
+template <int QU, int MODE>
+__global__ __launch_bounds__(64 * QW) void k_quantize_q8k(QuantArgs a) {
+#pragma clang fp contract(off)
   __shared__ float s_wmax[QW];
+  __shared__ double s_ss[QW];
+  __shared__ float s_dz[MODE == Q_RMSNORM ? RMS_SBMAX : 1];
+  __shared__ float s_r;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t m = blockIdx.x;
-  const int64_t src_row = rows ? (int64_t)rows[m] : m;
-  const float* xrow = x + src_row * ldx;
+  const int64_t m = blockIdx.x, SB = a.SB, K = SB * QK;
+  const int64_t src_row = (MODE == Q_PLAIN && a.rows) ? (int64_t)a.rows[m] : m;
+  const float* xrow = a.x + src_row * a.ldx;
   // every lane's 16 bytes are aligned exactly when the row start is
-  const bool vec = ((((uintptr_t)xrow) & 15) == 0);
+  const bool vec = ((((uintptr_t)xrow) & 15) == 0) && (MODE != Q_SWIGLU || (K & 3) == 0);
+  uint8_t* yrow = a.y + m * SB * Q8K_BYTES;
   float wmax = 0.0f;
+  double ss = 0.0;
   for (int64_t sb0 = wv; sb0 < SB; sb0 += QW * QU) {
     float v[QU][4];
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const int64_t sb = sb0 + QW * u < SB ? sb0 + QW * u : SB - 1;
-      const float* xb = xrow + sb * QK + 4 * lane;
-      if (vec) {
-        const float4 t = *(const float4*)xb;
-        v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
-      } else {
+      load4(xrow + sb * QK + 4 * lane, vec, v[u]);
+      if constexpr (MODE == Q_RMSNORM) {
+        float gv[4];
+        load4(a.g + sb * QK + 4 * lane, (((uintptr_t)a.g) & 15) == 0, gv);
+        const bool live = sb0 + QW * u < SB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[u][i] = xb[i];
+        for (int i = 0; i < 4; ++i) {
+          ss += live ? (double)v[u][i] * (double)v[u][i] : 0.0;
+          v[u][i] = v[u][i] * gv[i];
+        }
+      } else if constexpr (MODE == Q_SWIGLU) {
+        float up[4];
+        load4(xrow + K + sb * QK + 4 * lane, vec, up);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double gd = (double)v[u][i];
+          v[u][i] = (float)(gd * (double)up[i] / (1.0 + exp(-gd)));
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const int64_t sb = sb0 + QW * u;
-      wmax = fmaxf(wmax, quantize_block(v[u], y + (m * SB + sb) * Q8K_BYTES, lane, sb < SB));
+      const float d = quantize_block(v[u], yrow + sb * Q8K_BYTES, lane, sb < SB, MODE != Q_RMSNORM);
+      if constexpr (MODE == Q_RMSNORM) {
+        if (lane == 0 && sb < SB) s_dz[sb] = d;
+      } else {
+        wmax = fmaxf(wmax, __builtin_fabsf(d));
+      }
     }
   }
-  if (dmax) {
+  if constexpr (MODE == Q_RMSNORM) {
+    // the row's factor r, then each block's d = r * d_z (r > 0, so the
+    // largest |d| is r times the largest |d_z| after rounding as well)
+    ss = wave_sum_f64(ss);
+    if (lane == 0) s_ss[wv] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int k = 0; k < QW; ++k) t += s_ss[k];
+      s_r = (float)(1.0 / sqrt(t / (double)K + (double)a.eps));
+    }
+    __syncthreads();
+    const float r = s_r;
+    for (int64_t sb = threadIdx.x; sb < SB; sb += 64 * QW) {
+      const float d = r * s_dz[sb];
+      *(float*)(yrow + sb * Q8K_BYTES) = d;
+      wmax = fmaxf(wmax, __builtin_fabsf(d));
+    }
+    if (a.dmax) {
+      // every block's d is written by threads of wave 0 (SB <= 64)
+      wmax = __builtin_bit_cast(float, wave_max_bits(__builtin_bit_cast(uint32_t, wmax)));
+      if (threadIdx.x == 0) a.dmax[m] = wmax;
+    }
+  } else if (a.dmax) {
     if (lane == 0) s_wmax[wv] = wmax;
     __syncthreads();
     if (threadIdx.x == 0) {
       float r = s_wmax[0];
 #pragma unroll
       for (int k = 1; k < QW; ++k) r = fmaxf(r, s_wmax[k]);
-      dmax[m] = r;
+      a.dmax[m] = r;
     }
   }
 }
 
-hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
-                               float* dmax, hipStream_t s) {
+template <int MODE>
+static hipError_t launch_mode(const QuantArgs& a, int64_t M, hipStream_t s) {
   // enough blocks in flight per wave to cover rows of up to 64 blocks in one
   // round (K = 4096: one per wave; K = 12288: three)
-  const int64_t per_wave = (SB + QW - 1) / QW;
+  const int64_t per_wave = (a.SB + QW - 1) / QW;
   const dim3 grid((unsigned)M), block(64 * QW);
   if (per_wave <= 1)
-    hipLaunchKernelGGL(k_quantize_q8k<1>, grid, block, 0, s, x, ldx, rows, SB, y, dmax);
+    hipLaunchKernelGGL((k_quantize_q8k<1, MODE>), grid, block, 0, s, a);
   else if (per_wave == 2)
-    hipLaunchKernelGGL(k_quantize_q8k<2>, grid, block, 0, s, x, ldx, rows, SB, y, dmax);
+    hipLaunchKernelGGL((k_quantize_q8k<2, MODE>), grid, block, 0, s, a);
   else if (per_wave == 3)
-    hipLaunchKernelGGL(k_quantize_q8k<3>, grid, block, 0, s, x, ldx, rows, SB, y, dmax);
+    hipLaunchKernelGGL((k_quantize_q8k<3, MODE>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(k_quantize_q8k<4>, grid, block, 0, s, x, ldx, rows, SB, y, dmax);
+    hipLaunchKernelGGL((k_quantize_q8k<4, MODE>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
+                               float* dmax, hipStream_t s) {
+  return launch_mode<Q_PLAIN>(QuantArgs{x, ldx, rows, SB, y, dmax, nullptr, 0.0f}, M, s);
+}
+
+bool rmsnorm_quantize_fits(int64_t SB) { return SB <= RMS_SBMAX; }
+
+hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, int64_t SB, const float* g, float eps,
+                                       uint8_t* y, float* dmax, hipStream_t s) {
+  return launch_mode<Q_RMSNORM>(QuantArgs{x, ldx, nullptr, SB, y, dmax, g, eps}, M, s);
+}
+
+hipError_t launch_swiglu_quantize_q8k(const float* gu, int64_t ldgu, int64_t M, int64_t SB, uint8_t* y, float* dmax,
+                                      hipStream_t s) {
+  return launch_mode<Q_SWIGLU>(QuantArgs{gu, ldgu, nullptr, SB, y, dmax, nullptr, 0.0f}, M, s);
 }
 
 }  // namespace dllm

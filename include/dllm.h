@@ -73,6 +73,36 @@ int dllm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
                       void *y_q8k, float *dmax, void *stream);
 
 /*
+ * Fused producers of the quantized activations (Technical Specification,
+ * "Transformer Execution": RMSNorm before the QKV and MLP projections, and a
+ * SwiGLU MLP; Development plan, "Model facts used": RMSNorm eps 1e-5, FFN
+ * 12288 SwiGLU; v0.2 goals: fused normalization).  Each writes what
+ * dllm_quantize_q8k writes for the producer's output, without the f32
+ * intermediate in memory.
+ *
+ * dllm_rmsnorm_quantize_q8k: per row of x (K values) with norm weight g [K],
+ *   r = f32(1 / sqrt(sum_k x_k^2 / K + eps)), the sum of squares in f64;
+ *   the records hold the codes and bsums of z = f32(x * g) (the block rule
+ *   above) and d = f32(r * d_z): the records of RMSNorm(x) * g with the
+ *   common factor r moved into each block's scale, so the codes are those of
+ *   z exactly and only d depends on r.  K <= 16384 (DLLM_E_SHAPE otherwise);
+ *   0 <= eps <= 1.  dmax as for dllm_quantize_q8k.
+ *   x f32 [M][ldx] and g f32 [K], 4-byte aligned; y_q8k [M][K/256] records.
+ *
+ * dllm_swiglu_quantize_q8k: per row of gu (f32 [M][ldgu], ldgu >= 2F), gate
+ *   = gu[m][0..F), up = gu[m][F..2F) (the layout of one GEMM over the
+ *   stacked gate and up weights); the records of act = f32(gate * up /
+ *   (1 + exp(-gate))) (silu(gate) * up, evaluated in f64 and rounded once);
+ *   F a positive multiple of 256; y_q8k [M][F/256] records.
+ */
+int dllm_rmsnorm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
+                              const float *g, float eps, void *y_q8k,
+                              float *dmax, void *stream);
+int dllm_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F,
+                             int64_t ldgu, void *y_q8k, float *dmax,
+                             void *stream);
+
+/*
  * Decode Q4_K / Q6_K super-blocks into the shared form both types reduce to
  * (Development plan, "Compute design", second bullet: unsigned bytes, an int16
  * scale per 16 and an f32 offset per 16; the super-block factor D is kept as a

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -122,6 +122,27 @@ def test_lmhead_confidence_argument_errors(dl):
     assert "dllm_lmhead_confidence" in dl.last_error()
     assert L.dllm_lmhead_confidence(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE,
                                     FAKE, FAKE, ws, ok_ws - 1, None) == dl.E_WORKSPACE
+
+
+def test_fused_producer_argument_errors(dl):
+    L = dl.lib
+    y = FAKE
+    # RMSNorm: K a multiple of 256 and at most 16384, ldx >= K, eps in [0, 1], g required
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 300, 300, FAKE, 1e-5, y, None, None) == dl.E_SHAPE
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 16640, 16640, FAKE, 1e-5, y, None, None) == dl.E_SHAPE
+    assert "16384" in dl.last_error()
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 512, 256, FAKE, 1e-5, y, None, None) == dl.E_ARG
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 512, 512, None, 1e-5, y, None, None) == dl.E_ARG
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 512, 512, FAKE, -1.0, y, None, None) == dl.E_ARG
+    assert L.dllm_rmsnorm_quantize_q8k(FAKE, 4, 512, 512, FAKE, float("nan"), y, None, None) == dl.E_ARG
+    assert L.dllm_rmsnorm_quantize_q8k(ctypes.c_void_p((1 << 20) + 2), 4, 512, 512, FAKE, 1e-5, y, None,
+                                       None) == dl.E_ALIGN
+    # SwiGLU: F a multiple of 256, the row holds gate and up (ldgu >= 2F)
+    assert L.dllm_swiglu_quantize_q8k(FAKE, 4, 100, 200, y, None, None) == dl.E_SHAPE
+    assert L.dllm_swiglu_quantize_q8k(FAKE, 4, 256, 511, y, None, None) == dl.E_ARG
+    assert "ldgu" in dl.last_error()
+    assert L.dllm_swiglu_quantize_q8k(None, 4, 256, 512, y, None, None) == dl.E_ARG
+    assert L.dllm_swiglu_quantize_q8k(FAKE, 0, 256, 512, y, None, None) == dl.E_SHAPE
 
 
 def test_workspace_queries(dl):

@@ -97,6 +97,68 @@ def test_quantize_q8k_edge_blocks(dl):
     assert dmax[0].item() == 0.0  # an all-zero row
 
 
+# ------------------------------------------------- fused producers ----
+def _split_records(xq, M, K):
+    r = xq.reshape(M, K // 256, 292)
+    d = np.ascontiguousarray(r[:, :, :4]).view(np.float32)[..., 0]
+    return d, r[:, :, 4:]  # block scales; codes and bsums (bytes 4..292)
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 256, 0), (37, 4096, 0), (148, 4096, 0), (148, 12288, 0), (9, 16384, 128)])
+def test_rmsnorm_quantize_q8k(dl, M, K, pad):
+    """RMSNorm -> Q8_K: codes and bsums bit-exact (those of x*g); each block
+    scale within 2 ulp of the oracle's (r's f64 sum of squares runs in another
+    order, which can move r by one f32 ulp); dmax exactly the largest |d|."""
+    _say(f"rmsnorm quantize M={M} K={K} pad={pad}")
+    x = synth.normal_f32((M, K + pad), 51, f"rms-{M}-{K}") * torch.logspace(-4, 4, M).unsqueeze(1)
+    g = synth.normal_f32((K,), 51, f"rms-g-{K}")
+    g[::97] = 0.0
+    if M > 2:
+        x[2, :] = 0.0  # an all-zero row: d = 0 everywhere
+    ref, ref_dmax = oracle.rmsnorm_quantize_q8k(x[:, :K].numpy(), g.numpy(), 1e-5)
+    dmax = torch.full((M,), -1.0, device=DEV)
+    got = dl.rmsnorm_quantize_q8k(x.to(DEV)[:, :K], g.to(DEV), 1e-5, dmax=dmax).cpu().numpy()
+    gd, gq = _split_records(got, M, K)
+    rd, rq = _split_records(ref, M, K)
+    assert np.array_equal(gq, rq), "codes / bsums differ"
+    assert np.all(np.abs(gd - rd) <= 2 * np.spacing(np.abs(rd).astype(np.float32))), "block scales beyond 2 ulp"
+    assert np.array_equal(dmax.cpu().numpy(), np.abs(gd).max(axis=1))
+    assert np.all(np.abs(dmax.cpu().numpy() - ref_dmax) <= 2 * np.spacing(ref_dmax))
+    _say(f"rmsnorm quantize: {np.count_nonzero(gd != rd)} of {gd.size} block scales differ from the oracle's by an ulp")
+
+
+@pytest.mark.parametrize("M,F,pad", [(1, 256, 0), (37, 2048, 0), (148, 12288, 0), (5, 1024, 64)])
+def test_swiglu_quantize_q8k(dl, M, F, pad):
+    """SwiGLU -> Q8_K: the records of f32(silu(gate) * up) evaluated in f64,
+    bit-exact, including gates of 0, +-1000 and 60; dmax exact."""
+    _say(f"swiglu quantize M={M} F={F} pad={pad}")
+    gu = synth.normal_f32((M, 2 * F + pad), 52, f"swiglu-{M}-{F}") * 3.0
+    gu[0, :4] = torch.tensor([0.0, -1000.0, 1000.0, 60.0])
+    ref, ref_dmax = oracle.swiglu_quantize_q8k(gu[:, :2 * F].numpy())
+    dmax = torch.full((M,), -1.0, device=DEV)
+    got = dl.swiglu_quantize_q8k(gu.to(DEV)[:, :2 * F], dmax=dmax).cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(dmax.cpu().numpy(), ref_dmax)
+
+
+def test_fused_producers_feed_the_gemm(dl):
+    """The fused records drive dllm_qgemm like any Q8_K input: whole oracle
+    rows of the down projection on SwiGLU records and of Q+K+V on RMSNorm
+    records (the GEMM's parity with the oracle's own records)."""
+    M, D, F = 20, 1024, 2048
+    gu = synth.normal_f32((M, 2 * F), 53, "feed-gu")
+    xs = synth.normal_f32((M, D), 53, "feed-x")
+    g = synth.normal_f32((D,), 53, "feed-g")
+    for qtype, N, K, xq_ref, xq_gpu in (
+            (12, 300, F, oracle.swiglu_quantize_q8k(gu.numpy())[0], dl.swiglu_quantize_q8k(gu.to(DEV))),
+            (14, 300, D, oracle.rmsnorm_quantize_q8k(xs.numpy(), g.numpy(), 1e-5)[0],
+             dl.rmsnorm_quantize_q8k(xs.to(DEV), g.to(DEV), 1e-5))):
+        w = _weights(qtype, N, K, 53, f"feed-w-{qtype}")
+        ref = oracle.gemm(qtype, w.numpy(), N, K, xq_ref, M)
+        y = dl.qgemm(qtype, w.to(DEV), N, K, xq_gpu, M).cpu().numpy()
+        assert_close_rows(y, ref, f"gemm on fused records qtype={qtype}")
+
+
 def test_gather_quantize_through_lmhead_equals_plain_quantize(dl):
     # the LM head's gather+quantize must feed the GEMM the same Q8_K bytes as
     # quantizing the gathered rows directly: compare logits with qgemm on them.
