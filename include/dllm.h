@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 3
+#define DLLM_ABI_VERSION 4
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
