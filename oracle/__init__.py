@@ -54,11 +54,14 @@ def lib():
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_q4k_fields.restype = None
         L.oracle_q4k_fields.argtypes = [P, P, P, P, P, P]
+        L.oracle_f16_round.restype = ctypes.c_double
+        L.oracle_f16_round.argtypes = [ctypes.c_float]
         L.oracle_q6k_fields.restype = None
         L.oracle_q6k_fields.argtypes = [P, P, P, P]
         for name, args in {
             "oracle_decode_rows": [I, P, I64, I64, P],
             "oracle_softmax_stats": [P, I64, I64, P, P],
+            "oracle_attention": [P, I64, I64, I64, I64, ctypes.c_double, P],
             "oracle_rmsnorm_quantize_q8k": [P, I64, I64, I64, P, ctypes.c_float, P, P],
             "oracle_swiglu_quantize_q8k": [P, I64, I64, I64, P, P],
             "oracle_decode_shared": [I, P, I64, P],
@@ -229,3 +232,18 @@ def swiglu_quantize_q8k(gu: np.ndarray):
     dmax = np.zeros(M, np.float32)
     _check(lib().oracle_swiglu_quantize_q8k(_p(gu), M, F, F2, _p(out), _p(dmax)), "swiglu_quantize_q8k")
     return out, dmax
+
+
+def f16_round(x: float) -> float:
+    """The nearest binary16 value of an f32 (ties to even), as a float."""
+    return lib().oracle_f16_round(float(x))
+
+
+def attention(qkv: np.ndarray, H: int, D: int, scale: float) -> np.ndarray:
+    """f64 [L, H*D]: bidirectional softmax attention per head over f16-rounded
+    Q, K, V taken from the rows of qkv (Q | K | V, H*D values each)."""
+    qkv = np.ascontiguousarray(qkv, np.float32)
+    L, ld = qkv.shape
+    out = np.zeros((L, H * D), np.float64)
+    _check(lib().oracle_attention(_p(qkv), L, ld, H, D, float(scale), _p(out)), "attention")
+    return out

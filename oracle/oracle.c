@@ -485,3 +485,59 @@ int oracle_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F, int64_t ld
   free(a);
   return 0;
 }
+
+/* ---- bidirectional attention ------------------------------------------- */
+/* f32 -> nearest binary16 value (ties to even), as a double: the quantum is
+ * 2^(e-10) for a value of exponent e >= -14 and 2^-24 below; magnitudes that
+ * round to 65520 or more overflow to infinity. */
+double oracle_f16_round(float x) {
+  const double a = fabs((double)x);
+  if (a == 0.0 || a != a) return (double)x;
+  int E;
+  (void)frexp(a, &E); /* a = f * 2^E, f in [0.5, 1): exponent E - 1 */
+  const int e = E - 1 < -14 ? -14 : E - 1;
+  const double quantum = ldexp(1.0, e - 10);
+  double r = rint(a / quantum) * quantum; /* a / quantum is exact; rint rounds half to even */
+  if (r >= 65520.0) r = INFINITY;
+  return x < 0 ? -r : r;
+}
+
+/* The pages' layer attends over the whole canvas (bidirectional, not causal)
+ * after the QKV projection, on f16 tensor cores with a softmax over the keys.
+ * Per head h and query i, with q, k, v rounded to f16 (the operand format):
+ *   s_j = scale * sum_d q_id k_jd,  p_j = exp(s_j - max s) / sum exp(s - max s),
+ *   out[i][h D + d] = sum_j p_j v_jd,
+ * in f64.  qkv rows hold Q (H*D values), then K, then V. */
+int oracle_attention(const float *qkv, int64_t L, int64_t ldqkv, int64_t H, int64_t D, double scale, double *out) {
+  if (L <= 0 || H <= 0 || D <= 0 || ldqkv < 3 * H * D) return -1;
+  /* the operands rounded to f16 once: r[(j * 3 + part) * H * D + h * D + d] */
+  double *r = (double *)malloc(sizeof(double) * (size_t)(L * 3 * H * D));
+  for (int64_t j = 0; j < L; ++j)
+    for (int64_t t = 0; t < 3 * H * D; ++t) r[j * 3 * H * D + t] = oracle_f16_round(qkv[j * ldqkv + t]);
+  double *s = (double *)malloc(sizeof(double) * (size_t)L);
+  for (int64_t h = 0; h < H; ++h)
+    for (int64_t i = 0; i < L; ++i) {
+      const double *q = r + i * 3 * H * D + h * D;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < L; ++j) {
+        const double *k = r + j * 3 * H * D + H * D + h * D;
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += q[d] * k[d];
+        s[j] = scale * acc;
+        if (s[j] > mx) mx = s[j];
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j < L; ++j) {
+        s[j] = exp(s[j] - mx);
+        z += s[j];
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < L; ++j) acc += s[j] * r[j * 3 * H * D + 2 * H * D + h * D + d];
+        out[i * H * D + h * D + d] = acc / z;
+      }
+    }
+  free(s);
+  free(r);
+  return 0;
+}
