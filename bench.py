@@ -274,9 +274,8 @@ def main():
         "quantize_q8k_after_swiglu": (lambda: dl.quantize_q8k(layers[0]["act"], xq_f, dmax_f),
                                       L * FFN * 4 + L * FFN // 256 * 292),
     }
-    fused_out = {}
-    for name, (fn, byts) in fused.items():
-        # per call as a node of a replayed graph of 20 calls, like the step's
+    def graph_node_ms(fn):
+        """Per call as a node of a replayed graph of 20 calls, like the step's."""
         fn()
         torch.cuda.synchronize()
         fg = torch.cuda.CUDAGraph()
@@ -297,8 +296,21 @@ def main():
             b.record()
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) / 20)
-        fms = sorted(times)[2]
+        return sorted(times)[2]
+
+    fused_out = {}
+    for name, (fn, byts) in fused.items():
+        fms = graph_node_ms(fn)
         fused_out[name] = {"avg_ms": round(fms, 5), "GBps": round(byts / (fms * 1e-3) / 1e9, 1)}
+
+    # bidirectional attention on the Q+K+V projection's output (not part of
+    # the step): 32 heads of 128 over the L-token canvas
+    attn_out = torch.empty((L, D), dtype=torch.float32, device=dev)
+    a_ms = graph_node_ms(lambda: dl.attention(y_qkv, 32, 128, None, attn_out))
+    a_flops = 4 * L * L * D
+    attention = {"avg_ms": round(a_ms, 5), "TFLOPs": round(a_flops / (a_ms * 1e-3) / 1e12, 2),
+                 "GBps": round((L * 3 * D * 4 + L * D * 4) / (a_ms * 1e-3) / 1e9, 1),
+                 "shape": f"L={L}, 32 heads x 128, f16 operands", "in_step": False}
     print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
     print(f"[bench] per-call shapes: " + json.dumps(shapes), file=sys.stderr, flush=True)
 
@@ -358,6 +370,7 @@ def main():
                               "outputs": "logits, argmax, log-sum-exp and p(argmax) per masked row",
                               "in_step": False},
         "fused_producers": dict(fused_out, in_step=False),
+        "attention": attention,
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),
     }

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libdllm.so")
 
 HEADER_EXPORTS = (
     "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_rmsnorm_quantize_q8k",
-    "dllm_swiglu_quantize_q8k", "dllm_decode_qk",
+    "dllm_swiglu_quantize_q8k", "dllm_attention", "dllm_decode_qk",
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
 )
@@ -53,6 +53,7 @@ def _load():
         "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
         "dllm_rmsnorm_quantize_q8k": (I, [P, I64, I64, I64, P, ctypes.c_float, P, P, P]),
         "dllm_swiglu_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
+        "dllm_attention": (I, [P, I64, I64, I64, I64, ctypes.c_float, P, I64, P]),
         "dllm_decode_qk": (I, [I, P, I64, P, P]),
         "dllm_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_qgemm": (I, [I, P, I64, I64, P, P, I64, P, I64, P, I64, P]),
@@ -150,6 +151,22 @@ def swiglu_quantize_q8k(gu: torch.Tensor, out: torch.Tensor | None = None,
     if dmax is not None:
         assert dmax.dtype == torch.float32 and dmax.is_contiguous() and dmax.numel() >= M
     _check(lib.dllm_swiglu_quantize_q8k(_ptr(gu), M, F, gu.stride(0), _ptr(out), _ptr(dmax), _stream(dev)))
+    return out
+
+
+def attention(qkv: torch.Tensor, H: int, D: int = 128, scale: float | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Bidirectional attention per head over the rows of qkv (Q | K | V, H*D
+    values each): f32 [L, H*D]."""
+    dev = _dev(qkv)
+    assert qkv.dtype == torch.float32 and qkv.dim() == 2 and qkv.stride(1) == 1
+    L = qkv.shape[0]
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((L, H * D), dtype=torch.float32, device=dev)
+    _check(lib.dllm_attention(_ptr(qkv), L, qkv.stride(0), H, D, float(scale), _ptr(out), out.stride(0),
+                              _stream(dev)))
     return out
 
 

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdllm.so")
-SOURCES = ["quantize.hip", "decode.hip", "qgemm.hip", "lmhead.hip", "abi.hip"]
+SOURCES = ["quantize.hip", "decode.hip", "qgemm.hip", "lmhead.hip", "attention.hip", "abi.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never let the compiler form v_pk_{add,mul,fma}_f32.

@@ -280,6 +280,27 @@ int dllm_swiglu_quantize_q8k(const float* gu, int64_t M, int64_t F, int64_t ldgu
                     "dllm_swiglu_quantize_q8k launch");
 }
 
+int dllm_attention(const float* qkv, int64_t L, int64_t ld_qkv, int64_t H, int64_t D, float scale, float* out,
+                   int64_t ld_out, void* stream) {
+  const char* fn = "dllm_attention";
+  if (!qkv || !out) return fail(DLLM_E_ARG, "%s: null pointer (qkv=%p, out=%p)", fn, (const void*)qkv, (void*)out);
+  if (H <= 0 || L <= 0) return fail(DLLM_E_SHAPE, "%s: need L > 0 and H > 0 (L=%lld, H=%lld)", fn, (long long)L,
+                                    (long long)H);
+  if (!attention_fits(L, D))
+    return fail(DLLM_E_SHAPE, "%s: head dimension %lld and L=%lld: this kernel takes D = 128 and 1 <= L <= 256 "
+                "(every key of a head held in LDS)", fn, (long long)D, (long long)L);
+  if (ld_qkv < 3 * H * D) return fail(DLLM_E_ARG, "%s: ld_qkv=%lld < 3*H*D=%lld", fn, (long long)ld_qkv,
+                                      (long long)(3 * H * D));
+  if (ld_out < H * D) return fail(DLLM_E_ARG, "%s: ld_out=%lld < H*D=%lld", fn, (long long)ld_out, (long long)(H * D));
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(DLLM_E_ARG, "%s: scale must be finite", fn);
+  if (!aligned(qkv, 16) || !aligned(out, 16) || ld_qkv % 4 || ld_out % 4)
+    return fail(DLLM_E_ALIGN, "%s: qkv and out must be 16-byte aligned with row strides a multiple of 4", fn);
+  if (H > 65535) return fail(DLLM_E_SHAPE, "%s: H=%lld exceeds 65535", fn, (long long)H);
+  return hip_status(launch_attention(qkv, L, ld_qkv, H, out, ld_out, scale, (hipStream_t)stream),
+                    "dllm_attention launch");
+}
+
 int dllm_decode_qk(int qtype, const void* w, int64_t n_superblocks, void* out, void* stream) {
   int rc = check_qtype(qtype);
   if (rc) return rc;

@@ -39,6 +39,10 @@ hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, i
                                        uint8_t* y, float* dmax, hipStream_t s);
 hipError_t launch_swiglu_quantize_q8k(const float* gu, int64_t ldgu, int64_t M, int64_t SB, uint8_t* y, float* dmax,
                                       hipStream_t s);
+// Bidirectional attention (attention.hip): head dimension 128, 1 <= L <= 256.
+bool attention_fits(int64_t L, int64_t D);
+hipError_t launch_attention(const float* qkv, int64_t L, int64_t ld, int64_t H, float* out, int64_t ldo, float scale,
+                            hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
 // cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
 // 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up

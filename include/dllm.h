@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 4
+#define DLLM_ABI_VERSION 5
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -101,6 +101,27 @@ int dllm_rmsnorm_quantize_q8k(const float *x, int64_t M, int64_t K, int64_t ldx,
 int dllm_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F,
                              int64_t ldgu, void *y_q8k, float *dmax,
                              void *stream);
+
+/*
+ * Bidirectional attention over the canvas (Technical Specification,
+ * "Transformer Execution" and "Critical difference from autoregressive
+ * execution": full, not causal, attention over the diffusion region; README,
+ * the GPU bullet: attention on the f16 tensor cores with a softmax over the
+ * keys).  Per head h and query i:
+ *   out[i][h D + d] = sum_j softmax_j(scale * q_i . k_j) v_jd
+ * over all L keys, with q, k, v rounded to f16 (round to nearest even) and the
+ * scores, softmax and sums in f32.
+ *   qkv  f32 [L][ld_qkv]: per row Q (H*D values, head h at h*D), then K, then
+ *        V -- the layout of one GEMM over the stacked Q, K, V weights
+ *   out  f32 [L][ld_out] (written: H*D values per row)
+ *   scale  finite (1/sqrt(D) for standard attention)
+ * D must be 128 and 1 <= L <= 256 (a head's keys stay in LDS): DLLM_E_SHAPE
+ * otherwise.  qkv and out 16-byte aligned, ld_qkv >= 3*H*D and ld_out >= H*D
+ * multiples of 4.  RoPE, if the model uses it, is applied to Q and K before.
+ */
+int dllm_attention(const float *qkv, int64_t L, int64_t ld_qkv, int64_t H,
+                   int64_t D, float scale, float *out, int64_t ld_out,
+                   void *stream);
 
 /*
  * Decode Q4_K / Q6_K super-blocks into the shared form both types reduce to

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +143,21 @@ def test_fused_producer_argument_errors(dl):
     assert "ldgu" in dl.last_error()
     assert L.dllm_swiglu_quantize_q8k(None, 4, 256, 512, y, None, None) == dl.E_ARG
     assert L.dllm_swiglu_quantize_q8k(FAKE, 0, 256, 512, y, None, None) == dl.E_SHAPE
+
+
+def test_attention_argument_errors(dl):
+    L = dl.lib
+    A = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never dereferenced
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 64, 0.1, A, 4096, None) == dl.E_SHAPE  # D != 128
+    assert "128" in dl.last_error()
+    assert L.dllm_attention(A, 257, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE  # L > 256
+    assert L.dllm_attention(A, 0, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE
+    assert L.dllm_attention(A, 148, 3 * 4096 - 4, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 128, 0.1, A, 4092, None) == dl.E_ARG
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 128, float("inf"), A, 4096, None) == dl.E_ARG
+    assert L.dllm_attention(ctypes.c_void_p((1 << 20) + 4), 148, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_ALIGN
+    assert L.dllm_attention(A, 148, 3 * 4096 + 2, 32, 128, 0.1, A, 4096, None) == dl.E_ALIGN
+    assert L.dllm_attention(None, 148, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
 
 
 def test_workspace_queries(dl):

@@ -159,6 +159,64 @@ def test_fused_producers_feed_the_gemm(dl):
         assert_close_rows(y, ref, f"gemm on fused records qtype={qtype}")
 
 
+# --------------------------------------------------------- attention ----
+def _attention_bound(qkv, L, H, D, scale):
+    """Per output, what the GPU may differ from the oracle (which uses the same
+    f16-rounded q, k, v): P rounded to f16 for the second product (2^-11
+    relative), the scores' f32 accumulation (at most ~128 * 2^-24 * scale *
+    sum|q||k|, entering the softmax weights doubled through exp), and f32
+    sums and division (well below both); in units of sum_j P_ij |v_jd|."""
+    r = qkv[:, :3 * H * D].astype(np.float16).astype(np.float64)
+    q = r[:, :H * D].reshape(L, H, D)
+    k = r[:, H * D:2 * H * D].reshape(L, H, D)
+    v = r[:, 2 * H * D:].reshape(L, H, D)
+    s = np.einsum("ihd,jhd->hij", q, k) * scale
+    p = np.exp(s - s.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    a = 130 * 2.0 ** -24 * abs(scale) * np.einsum("ihd,jhd->hij", np.abs(q), np.abs(k)).max(axis=2)  # [h, i]
+    pv = np.einsum("hij,jhd->ihd", p, np.abs(v))  # [i, h, d]
+    f = (2.0 ** -11 + np.expm1(2 * a).T[:, :, None] + 2.0 ** -20)
+    return (pv * f).reshape(L, H * D)
+
+
+@pytest.mark.parametrize("L,H,spread,pad", [(1, 1, 1.0, 0), (17, 3, 1.0, 4), (64, 2, 3.0, 0), (148, 32, 1.0, 0),
+                                            (148, 4, 4.0, 8), (200, 2, 0.3, 0), (256, 2, 1.0, 0)])
+def test_attention(dl, L, H, spread, pad):
+    """Bidirectional attention against the oracle on the same f16-rounded
+    operands, within the bound of the GPU's own roundings; from the layout of
+    a fused Q+K+V projection (with row padding), at soft and peaked softmaxes
+    and every key count from one to 256."""
+    D = 128
+    _say(f"attention L={L} H={H} spread={spread} pad={pad}")
+    qkv = synth.normal_f32((L, 3 * H * D + pad), 71, f"att-{L}-{H}-{pad}") * spread
+    scale = D ** -0.5
+    ref = oracle.attention(qkv[:, :3 * H * D].numpy(), H, D, scale)
+    got = dl.attention(qkv.to(DEV), H, D, scale).cpu().numpy().astype(np.float64)
+    bound = _attention_bound(qkv.numpy(), L, H, D, scale)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"attention: worst err/bound {np.max(err / bound):.3g}"
+    _say(f"attention L={L} H={H}: max err/bound = {np.max(err / bound):.3g}, max rel err "
+         f"{np.max(err / (np.abs(ref) + 1e-30)):.2e}")
+
+
+def test_attention_strided_output_and_bidirectional(dl):
+    """A strided output leaves its padding alone; query 0 follows a change in
+    the last key's value (no causal mask)."""
+    L, H, D = 100, 2, 128
+    qkv = synth.normal_f32((L, 3 * H * D), 72, "att-strided")
+    big = torch.full((L, H * D + 12), 7.0, device=DEV)
+    dl.attention(qkv.to(DEV), H, D, out=big[:, :H * D])
+    q2 = qkv.clone()
+    q2[L - 1, 2 * H * D:] += 5.0
+    o2 = dl.attention(q2.to(DEV), H, D)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, H * D:] == 7.0)
+    assert not torch.allclose(big[0, :H * D], o2[0])
+    ref = oracle.attention(qkv.numpy(), H, D, D ** -0.5)
+    bound = _attention_bound(qkv.numpy(), L, H, D, D ** -0.5)
+    assert np.all(np.abs(big[:, :H * D].cpu().numpy() - ref) <= bound)
+
+
 def test_gather_quantize_through_lmhead_equals_plain_quantize(dl):
     # the LM head's gather+quantize must feed the GEMM the same Q8_K bytes as
     # quantizing the gathered rows directly: compare logits with qgemm on them.
