@@ -179,13 +179,14 @@ def _attention_bound(qkv, L, H, D, scale):
     return (pv * f).reshape(L, H * D)
 
 
-@pytest.mark.parametrize("L,H,spread,pad", [(1, 1, 1.0, 0), (17, 3, 1.0, 4), (64, 2, 3.0, 0), (148, 32, 1.0, 0),
-                                            (148, 4, 4.0, 8), (200, 2, 0.3, 0), (256, 2, 1.0, 0)])
+@pytest.mark.parametrize("L,H,spread,pad", [(1, 1, 1.0, 0), (17, 3, 1.0, 4), (64, 2, 3.0, 0), (80, 3, 1.0, 0),
+                                            (100, 2, 2.0, 0), (148, 32, 1.0, 0), (148, 4, 4.0, 8), (176, 2, 2.0, 4),
+                                            (200, 2, 0.3, 0), (256, 2, 1.0, 0)])
 def test_attention(dl, L, H, spread, pad):
     """Bidirectional attention against the oracle on the same f16-rounded
     operands, within the bound of the GPU's own roundings; from the layout of
     a fused Q+K+V projection (with row padding), at soft and peaked softmaxes
-    and every key count from one to 256."""
+    and key counts from one to 256 (every count of 32-key chunks, 1 to 8)."""
     D = 128
     _say(f"attention L={L} H={H} spread={spread} pad={pad}")
     qkv = synth.normal_f32((L, 3 * H * D + pad), 71, f"att-{L}-{H}-{pad}") * spread
