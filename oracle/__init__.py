@@ -61,7 +61,7 @@ def lib():
         for name, args in {
             "oracle_decode_rows": [I, P, I64, I64, P],
             "oracle_softmax_stats": [P, I64, I64, P, P],
-            "oracle_attention": [P, I64, I64, I64, I64, ctypes.c_double, P],
+            "oracle_attention": [P, I64, I64, I64, I64, I64, ctypes.c_double, P],
             "oracle_rmsnorm_quantize_q8k": [P, I64, I64, I64, P, ctypes.c_float, P, P],
             "oracle_swiglu_quantize_q8k": [P, I64, I64, I64, P, P],
             "oracle_decode_shared": [I, P, I64, P],
@@ -152,22 +152,28 @@ def dequant_q8k(xq, M: int, K: int) -> np.ndarray:
     return out
 
 
-def gemm(qtype: int, w, N: int, K: int, xq, M: int, nthreads: int | None = None) -> np.ndarray:
-    """f64 y [M, N] = W_hat X_hat^T."""
+def gemm(qtype: int, w, N: int, K: int, xq, M: int, nthreads: int | None = None, bias=None) -> np.ndarray:
+    """f64 y [M, N] = W_hat X_hat^T, plus the f32 bias [N] of every row when
+    given (the Q, K, V projections of Dream-7B, README milestones: "QKV
+    bias"), added in f64."""
     w = _u8(w); xq = _u8(xq)
     y = np.zeros((M, N), np.float64)
     nt = nthreads or default_threads()
     _check(lib().oracle_gemm(qtype, _p(w), N, K, _p(xq), M, _p(y), nt), "gemm")
+    if bias is not None:
+        y += np.asarray(bias, np.float32).astype(np.float64)[None, :N]
     return y
 
 
-def gemm_sample(qtype: int, w, N: int, K: int, xq, M: int, mi, ni) -> np.ndarray:
-    """f64 y[mi[t], ni[t]] for each t."""
+def gemm_sample(qtype: int, w, N: int, K: int, xq, M: int, mi, ni, bias=None) -> np.ndarray:
+    """f64 y[mi[t], ni[t]] for each t (plus bias[ni[t]] when given)."""
     w = _u8(w); xq = _u8(xq)
     mi = np.ascontiguousarray(mi, np.int64); ni = np.ascontiguousarray(ni, np.int64)
     out = np.zeros(mi.size, np.float64)
     _check(lib().oracle_gemm_sample(qtype, _p(w), N, K, _p(xq), M, _p(mi), _p(ni),
                                     mi.size, _p(out)), "gemm_sample")
+    if bias is not None:
+        out += np.asarray(bias, np.float32).astype(np.float64)[ni]
     return out
 
 
@@ -239,11 +245,14 @@ def f16_round(x: float) -> float:
     return lib().oracle_f16_round(float(x))
 
 
-def attention(qkv: np.ndarray, H: int, D: int, scale: float) -> np.ndarray:
+def attention(qkv: np.ndarray, H: int, D: int, scale: float, Hkv: int | None = None) -> np.ndarray:
     """f64 [L, H*D]: bidirectional softmax attention per head over f16-rounded
-    Q, K, V taken from the rows of qkv (Q | K | V, H*D values each)."""
+    Q, K, V taken from the rows of qkv (Q of H heads | K of Hkv heads | V of
+    Hkv heads, D values per head; Hkv = H unless given).  Query head h reads
+    key/value head h // (H // Hkv)."""
+    Hkv = H if Hkv is None else Hkv
     qkv = np.ascontiguousarray(qkv, np.float32)
     L, ld = qkv.shape
     out = np.zeros((L, H * D), np.float64)
-    _check(lib().oracle_attention(_p(qkv), L, ld, H, D, float(scale), _p(out)), "attention")
+    _check(lib().oracle_attention(_p(qkv), L, ld, H, Hkv, D, float(scale), _p(out)), "attention")
     return out

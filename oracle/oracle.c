@@ -507,20 +507,28 @@ double oracle_f16_round(float x) {
  * Per head h and query i, with q, k, v rounded to f16 (the operand format):
  *   s_j = scale * sum_d q_id k_jd,  p_j = exp(s_j - max s) / sum exp(s - max s),
  *   out[i][h D + d] = sum_j p_j v_jd,
- * in f64.  qkv rows hold Q (H*D values), then K, then V. */
-int oracle_attention(const float *qkv, int64_t L, int64_t ldqkv, int64_t H, int64_t D, double scale, double *out) {
-  if (L <= 0 || H <= 0 || D <= 0 || ldqkv < 3 * H * D) return -1;
-  /* the operands rounded to f16 once: r[(j * 3 + part) * H * D + h * D + d] */
-  double *r = (double *)malloc(sizeof(double) * (size_t)(L * 3 * H * D));
+ * in f64.  qkv rows hold Q (H heads of D values), then K, then V (Hkv heads
+ * each).  With grouped-query attention (Dream-7B, README milestones: "GQA"),
+ * Hkv divides H and query head h reads key/value head h / (H / Hkv); Hkv = H
+ * is plain multi-head attention. */
+int oracle_attention(const float *qkv, int64_t L, int64_t ldqkv, int64_t H, int64_t Hkv, int64_t D, double scale,
+                     double *out) {
+  if (L <= 0 || H <= 0 || Hkv <= 0 || H % Hkv || D <= 0) return -1;
+  const int64_t W = (H + 2 * Hkv) * D; /* Q of H heads, then K and V of Hkv heads */
+  if (ldqkv < W) return -1;
+  const int64_t G = H / Hkv;            /* query heads per key/value head */
+  /* the operands rounded to f16 once: r[j * W + t] */
+  double *r = (double *)malloc(sizeof(double) * (size_t)(L * W));
   for (int64_t j = 0; j < L; ++j)
-    for (int64_t t = 0; t < 3 * H * D; ++t) r[j * 3 * H * D + t] = oracle_f16_round(qkv[j * ldqkv + t]);
+    for (int64_t t = 0; t < W; ++t) r[j * W + t] = oracle_f16_round(qkv[j * ldqkv + t]);
   double *s = (double *)malloc(sizeof(double) * (size_t)L);
-  for (int64_t h = 0; h < H; ++h)
+  for (int64_t h = 0; h < H; ++h) {
+    const int64_t koff = H * D + (h / G) * D, voff = H * D + Hkv * D + (h / G) * D;
     for (int64_t i = 0; i < L; ++i) {
-      const double *q = r + i * 3 * H * D + h * D;
+      const double *q = r + i * W + h * D;
       double mx = -INFINITY;
       for (int64_t j = 0; j < L; ++j) {
-        const double *k = r + j * 3 * H * D + H * D + h * D;
+        const double *k = r + j * W + koff;
         double acc = 0.0;
         for (int64_t d = 0; d < D; ++d) acc += q[d] * k[d];
         s[j] = scale * acc;
@@ -533,10 +541,11 @@ int oracle_attention(const float *qkv, int64_t L, int64_t ldqkv, int64_t H, int6
       }
       for (int64_t d = 0; d < D; ++d) {
         double acc = 0.0;
-        for (int64_t j = 0; j < L; ++j) acc += s[j] * r[j * 3 * H * D + 2 * H * D + h * D + d];
+        for (int64_t j = 0; j < L; ++j) acc += s[j] * r[j * W + voff + d];
         out[i * H * D + h * D + d] = acc / z;
       }
     }
+  }
   free(s);
   free(r);
   return 0;

@@ -34,5 +34,5 @@ int oracle_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F, int64_t ld
                                uint8_t *out, float *dmax);
 double oracle_f16_round(float x);
 int oracle_attention(const float *qkv, int64_t L, int64_t ldqkv, int64_t H,
-                     int64_t D, double scale, double *out);
+                     int64_t Hkv, int64_t D, double scale, double *out);
 #endif

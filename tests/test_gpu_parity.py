@@ -403,21 +403,22 @@ def test_qgemm_deterministic(dl):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("M", [148, 160])
 @pytest.mark.parametrize("qtype,N,K", [(12, 24576, 4096), (12, 12288, 4096), (12, 8192, 4096), (12, 4096, 4096),
                                         (14, 4096, 4096), (12, 4096, 12288), (14, 4096, 12288)])
-def test_qgemm_step_shapes_at_148_tokens(dl, qtype, N, K):
-    """Every linear-layer shape of the LLaDA-8B step at L = 148, in the launch
+def test_qgemm_step_shapes(dl, qtype, N, K, M):
+    """Every linear-layer shape of the LLaDA-8B step at L = 148 and at L = 160
+    (the canvas of 32 prompt + 128 generated tokens), in the launch
     configuration the step uses (tuned tile and K split, with workspace):
     whole oracle rows for five tokens spread over both token tiles."""
-    M = 148
-    _say(f"step shape qtype={qtype} N={N} K={K}")
+    _say(f"step shape qtype={qtype} N={N} K={K} M={M}")
     w = _weights(qtype, N, K, 21, f"step-{qtype}-{N}-{K}")
-    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 21, f"step-x-{K}").numpy())
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 21, f"step-x-{K}-{M}").numpy())
     ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     wd, xd = w.to(DEV), torch.from_numpy(xq).to(DEV)
     dmax = torch.from_numpy(_dmax(xq, M, K)).to(DEV)
     y = dl.qgemm(qtype, wd, N, K, xd, M, workspace=ws, x_dmax=dmax)
-    toks = [0, 63, 79, 80, 147]
+    toks = [0, 63, 79, 80, M - 1]
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq[toks], len(toks))
     assert_close_rows(y.cpu().numpy()[toks], ref, f"step shape {qtype} {N}x{K}")
     # the per-token scale summary only spares the kernel its own scan
@@ -627,14 +628,16 @@ def test_lmhead_confidence(dl, monkeypatch, qtype, tiled, scale):
                       f"confidence qtype={qtype} tiled={tiled} scale={scale}")
 
 
-def test_lmhead_full_size(dl):
-    """Masked-row LM head: 32 masked canvas rows (20..51 of 148) x LLaDA's
-    untied 126464 x 4096 output matrix in Q6_K, against the full oracle."""
-    N, K, M = 126464, 4096, 148
-    _say("full-size lmhead")
+@pytest.mark.parametrize("M,first", [(148, 20), (160, 128)])
+def test_lmhead_full_size(dl, M, first):
+    """Masked-row LM head: 32 masked canvas rows (20..51 of 148, or the last
+    block 128..159 of a 32 + 128 canvas of 160) x LLaDA's untied 126464 x 4096
+    output matrix in Q6_K, against the full oracle."""
+    N, K = 126464, 4096
+    _say(f"full-size lmhead M={M} rows {first}..{first + 31}")
     w = _weights(14, N, K, 42, "output")
-    h = synth.normal_f32((M, K), 42, "hidden")
-    rows = torch.arange(20, 52, dtype=torch.int32)
+    h = synth.normal_f32((M, K), 42, f"hidden-{M}")
+    rows = torch.arange(first, first + 32, dtype=torch.int32)
     ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
     logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
     logits = logits.cpu().numpy(); am = am.cpu().numpy()

@@ -6,7 +6,10 @@ after the QKV projection, on f16 tensor cores with a softmax over the keys
 difference from autoregressive execution"; README, the GPU bullet).  The
 oracle's definition: f16-rounded Q, K, V (the operand format), scores, softmax
 and weighted sum in f64.  Pinned by numpy's float16 rounding, closed forms,
-key-permutation invariance and an independent numpy/scipy evaluation."""
+key-permutation invariance and an independent numpy/scipy evaluation.  The
+grouped-query form (Dream-7B, README milestones: "GQA") is pinned against
+numpy with repeated key/value heads, against multi-head attention on heads
+written out per query head, and by which query heads a key/value head feeds."""
 import numpy as np
 from scipy.special import softmax
 
@@ -82,3 +85,55 @@ def test_attention_is_bidirectional_and_permutation_invariant():
     changed = qkv.copy()
     changed[L - 1, 2 * H * D:] += 3.0
     assert not np.allclose(oracle.attention(changed, H, D, 0.5)[0], base[0])
+
+
+def _numpy_gqa(qkv, H, Hkv, D, scale):
+    """Grouped-query attention as multi-head attention on K and V repeated per
+    query head (np.repeat: key/value head h // G serves query heads h)."""
+    L = qkv.shape[0]
+    r = qkv.astype(np.float16).astype(np.float64)
+    q = r[:, :H * D].reshape(L, H, D)
+    k = np.repeat(r[:, H * D:(H + Hkv) * D].reshape(L, Hkv, D), H // Hkv, axis=1)
+    v = np.repeat(r[:, (H + Hkv) * D:(H + 2 * Hkv) * D].reshape(L, Hkv, D), H // Hkv, axis=1)
+    s = np.einsum("ihd,jhd->hij", q, k) * scale
+    p = softmax(s, axis=2)
+    return np.einsum("hij,jhd->ihd", p, v).reshape(L, H * D)
+
+
+def test_gqa_against_numpy_and_scipy():
+    rng = np.random.default_rng(65)
+    for L, H, Hkv, D in ((5, 4, 2, 8), (13, 6, 3, 16), (9, 7, 1, 8), (11, 3, 3, 16)):
+        qkv = rng.standard_normal((L, (H + 2 * Hkv) * D + 3)).astype(np.float32) * 1.5
+        got = oracle.attention(qkv, H, D, D ** -0.5, Hkv=Hkv)
+        assert np.allclose(got, _numpy_gqa(qkv[:, :(H + 2 * Hkv) * D], H, Hkv, D, D ** -0.5), rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_equals_mha_on_replicated_heads():
+    """GQA over Hkv heads equals plain attention over a Q+K+V row in which each
+    key/value head is written out once per query head of its group."""
+    rng = np.random.default_rng(66)
+    L, H, Hkv, D = 10, 6, 2, 8
+    G = H // Hkv
+    qkv = rng.standard_normal((L, (H + 2 * Hkv) * D)).astype(np.float32)
+    q = qkv[:, :H * D]
+    k = qkv[:, H * D:(H + Hkv) * D].reshape(L, Hkv, D)
+    v = qkv[:, (H + Hkv) * D:].reshape(L, Hkv, D)
+    k_full = np.concatenate([k[:, h // G] for h in range(H)], axis=1)
+    v_full = np.concatenate([v[:, h // G] for h in range(H)], axis=1)
+    mha = np.concatenate([q, k_full, v_full], axis=1)
+    assert np.array_equal(oracle.attention(qkv, H, D, 0.3, Hkv=Hkv), oracle.attention(mha, H, D, 0.3))
+
+
+def test_gqa_group_mapping():
+    """Changing key/value head 1 changes exactly the query heads G .. 2G-1."""
+    rng = np.random.default_rng(67)
+    L, H, Hkv, D = 8, 6, 3, 8
+    G = H // Hkv
+    qkv = rng.standard_normal((L, (H + 2 * Hkv) * D)).astype(np.float32)
+    base = oracle.attention(qkv, H, D, 0.5, Hkv=Hkv).reshape(L, H, D)
+    q2 = qkv.copy()
+    q2[:, (H + Hkv + 1) * D:(H + Hkv + 2) * D] += 3.0  # V of key/value head 1
+    q2[:, (H + 1) * D:(H + 2) * D] -= 1.0               # K of key/value head 1
+    got = oracle.attention(q2, H, D, 0.5, Hkv=Hkv).reshape(L, H, D)
+    changed = [h for h in range(H) if not np.array_equal(got[:, h], base[:, h])]
+    assert changed == list(range(G, 2 * G))

@@ -62,12 +62,17 @@ def test_exact_rational_brute_force(qtype, seed):
             b, v, _ = _rand_q8k(rng); bl.append(b); vl += v
         xrows.append(np.concatenate(bl)); xvals.append(vl)
     y = oracle.gemm(qtype, np.stack(wrows), N, K, np.stack(xrows), M)
+    # the same product with a bias per output feature (Dream-7B's QKV bias)
+    bias = (rng.standard_normal(N) * 10.0).astype(np.float32)
+    yb = oracle.gemm(qtype, np.stack(wrows), N, K, np.stack(xrows), M, bias=bias)
     for m in range(M):
         for n in range(N):
             terms = [a * b for a, b in zip(wvals[n], xvals[m])]
             exact = sum(terms)
             bound = sum(abs(t) for t in terms) * Fraction(1, 2 ** 50)
             assert abs(Fraction(y[m, n]) - exact) <= bound
+            exact_b = exact + Fraction(float(bias[n]))
+            assert abs(Fraction(yb[m, n]) - exact_b) <= bound + abs(exact_b) * Fraction(1, 2 ** 52)
 
 
 @pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q6_K])
@@ -114,6 +119,19 @@ def test_zero_weights_give_zero():
     w = np.zeros((N, K // 256 * 144), np.uint8)
     x = synth.normal_f32((M, K), 1, "x").numpy()
     assert not oracle.gemm(oracle.Q4_K, w, N, K, oracle.quantize_q8k(x), M).any()
+
+
+def test_zero_weights_with_bias_give_the_bias():
+    """Every token's row is the bias itself, feature by feature (not a
+    transposed or token-indexed bias)."""
+    N, M, K = 7, 3, 256
+    w = np.zeros((N, K // 256 * 210), np.uint8)
+    xq = oracle.quantize_q8k(synth.normal_f32((M, K), 2, "x").numpy())
+    bias = np.float32([1.5, -2.25, 3e-8, 0.0, -7e4, 0.1, 42.0])
+    y = oracle.gemm(oracle.Q6_K, w, N, K, xq, M, bias=bias)
+    assert np.array_equal(y, np.tile(bias.astype(np.float64), (M, 1)))
+    mi = np.array([0, 2, 1, 2]); ni = np.array([6, 0, 4, 1])
+    assert np.array_equal(oracle.gemm_sample(oracle.Q6_K, w, N, K, xq, M, mi, ni, bias=bias), y[mi, ni])
 
 
 @pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q6_K])
