@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libdllm.so")
 HEADER_EXPORTS = (
     "dllm_abi_version", "dllm_last_error", "dllm_quantize_q8k", "dllm_rmsnorm_quantize_q8k",
     "dllm_swiglu_quantize_q8k", "dllm_attention", "dllm_decode_qk",
-    "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_lmhead_workspace_bytes",
+    "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_qgemm_bias", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
 )
 
@@ -53,10 +53,11 @@ def _load():
         "dllm_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
         "dllm_rmsnorm_quantize_q8k": (I, [P, I64, I64, I64, P, ctypes.c_float, P, P, P]),
         "dllm_swiglu_quantize_q8k": (I, [P, I64, I64, I64, P, P, P]),
-        "dllm_attention": (I, [P, I64, I64, I64, I64, ctypes.c_float, P, I64, P]),
+        "dllm_attention": (I, [P, I64, I64, I64, I64, I64, ctypes.c_float, P, I64, P]),
         "dllm_decode_qk": (I, [I, P, I64, P, P]),
         "dllm_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_qgemm": (I, [I, P, I64, I64, P, P, I64, P, I64, P, I64, P]),
+        "dllm_qgemm_bias": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P, I64, P]),
         "dllm_lmhead_workspace_bytes": (I64, [I, I64, I64, I64]),
         "dllm_lmhead_masked": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, I64, P]),
         "dllm_lmhead_confidence": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, P]),
@@ -155,17 +156,19 @@ def swiglu_quantize_q8k(gu: torch.Tensor, out: torch.Tensor | None = None,
 
 
 def attention(qkv: torch.Tensor, H: int, D: int = 128, scale: float | None = None,
-              out: torch.Tensor | None = None) -> torch.Tensor:
-    """Bidirectional attention per head over the rows of qkv (Q | K | V, H*D
-    values each): f32 [L, H*D]."""
+              out: torch.Tensor | None = None, H_kv: int | None = None) -> torch.Tensor:
+    """Bidirectional attention per query head over the rows of qkv (Q of H
+    heads | K of H_kv heads | V of H_kv heads, D values per head; H_kv = H
+    unless given): f32 [L, H*D]."""
     dev = _dev(qkv)
     assert qkv.dtype == torch.float32 and qkv.dim() == 2 and qkv.stride(1) == 1
     L = qkv.shape[0]
+    H_kv = H if H_kv is None else H_kv
     if scale is None:
         scale = D ** -0.5
     if out is None:
         out = torch.empty((L, H * D), dtype=torch.float32, device=dev)
-    _check(lib.dllm_attention(_ptr(qkv), L, qkv.stride(0), H, D, float(scale), _ptr(out), out.stride(0),
+    _check(lib.dllm_attention(_ptr(qkv), L, qkv.stride(0), H, H_kv, D, float(scale), _ptr(out), out.stride(0),
                               _stream(dev)))
     return out
 
@@ -193,10 +196,11 @@ def qgemm_workspace(qtype: int, N: int, K: int, M: int, device) -> torch.Tensor:
 
 def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: int,
           y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-          x_dmax: torch.Tensor | None = None) -> torch.Tensor:
-    """y[M, N] (f32) = dequant(x_q8k) @ dequant(w)^T.  `y` may be a row-strided
-    view; `workspace` (uint8, >= qgemm_workspace_bytes) enables the K split;
-    `x_dmax` (f32 [M], from quantize_q8k) spares the kernel its own scan."""
+          x_dmax: torch.Tensor | None = None, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] (f32) = dequant(x_q8k) @ dequant(w)^T (+ bias[N], f32, through
+    dllm_qgemm_bias when given).  `y` may be a row-strided view; `workspace`
+    (uint8, >= qgemm_workspace_bytes) enables the K split; `x_dmax` (f32 [M],
+    from quantize_q8k) spares the kernel its own scan."""
     dev = _dev(w)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -204,8 +208,13 @@ def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: i
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if x_dmax is not None:
         assert x_dmax.dtype == torch.float32 and x_dmax.is_contiguous() and x_dmax.numel() >= M
-    _check(lib.dllm_qgemm(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(y), y.stride(0),
-                          _ptr(workspace), wsb, _stream(dev)))
+    if bias is None:
+        _check(lib.dllm_qgemm(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(y), y.stride(0),
+                              _ptr(workspace), wsb, _stream(dev)))
+    else:
+        assert bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() >= N
+        _check(lib.dllm_qgemm_bias(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(bias), _ptr(y),
+                                   y.stride(0), _ptr(workspace), wsb, _stream(dev)))
     return y
 
 

@@ -280,24 +280,26 @@ int dllm_swiglu_quantize_q8k(const float* gu, int64_t M, int64_t F, int64_t ldgu
                     "dllm_swiglu_quantize_q8k launch");
 }
 
-int dllm_attention(const float* qkv, int64_t L, int64_t ld_qkv, int64_t H, int64_t D, float scale, float* out,
-                   int64_t ld_out, void* stream) {
+int dllm_attention(const float* qkv, int64_t L, int64_t ld_qkv, int64_t H, int64_t H_kv, int64_t D, float scale,
+                   float* out, int64_t ld_out, void* stream) {
   const char* fn = "dllm_attention";
   if (!qkv || !out) return fail(DLLM_E_ARG, "%s: null pointer (qkv=%p, out=%p)", fn, (const void*)qkv, (void*)out);
-  if (H <= 0 || L <= 0) return fail(DLLM_E_SHAPE, "%s: need L > 0 and H > 0 (L=%lld, H=%lld)", fn, (long long)L,
-                                    (long long)H);
+  if (H <= 0 || L <= 0 || H_kv <= 0 || H % H_kv)
+    return fail(DLLM_E_SHAPE, "%s: need L > 0, H > 0 and H_kv > 0 dividing H (L=%lld, H=%lld, H_kv=%lld)", fn,
+                (long long)L, (long long)H, (long long)H_kv);
   if (!attention_fits(L, D))
     return fail(DLLM_E_SHAPE, "%s: head dimension %lld and L=%lld: this kernel takes D = 128 and 1 <= L <= 256 "
                 "(every key of a head held in LDS)", fn, (long long)D, (long long)L);
-  if (ld_qkv < 3 * H * D) return fail(DLLM_E_ARG, "%s: ld_qkv=%lld < 3*H*D=%lld", fn, (long long)ld_qkv,
-                                      (long long)(3 * H * D));
+  if (ld_qkv < (H + 2 * H_kv) * D)
+    return fail(DLLM_E_ARG, "%s: ld_qkv=%lld < (H + 2*H_kv)*D=%lld", fn, (long long)ld_qkv,
+                (long long)((H + 2 * H_kv) * D));
   if (ld_out < H * D) return fail(DLLM_E_ARG, "%s: ld_out=%lld < H*D=%lld", fn, (long long)ld_out, (long long)(H * D));
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return fail(DLLM_E_ARG, "%s: scale must be finite", fn);
   if (!aligned(qkv, 16) || !aligned(out, 16) || ld_qkv % 4 || ld_out % 4)
     return fail(DLLM_E_ALIGN, "%s: qkv and out must be 16-byte aligned with row strides a multiple of 4", fn);
   if (H > 65535) return fail(DLLM_E_SHAPE, "%s: H=%lld exceeds 65535", fn, (long long)H);
-  return hip_status(launch_attention(qkv, L, ld_qkv, H, out, ld_out, scale, (hipStream_t)stream),
+  return hip_status(launch_attention(qkv, L, ld_qkv, H, H_kv, out, ld_out, scale, (hipStream_t)stream),
                     "dllm_attention launch");
 }
 
@@ -332,13 +334,16 @@ static int check_gemm_args(const char* fn, int qtype, const void* w, int64_t N, 
   return DLLM_OK;
 }
 
-int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax, int64_t M,
-               float* y, int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
-  int rc = check_gemm_args("dllm_qgemm", qtype, w, N, K, x_q8k, M);
+// dllm_qgemm, and with a bias dllm_qgemm_bias.
+static int qgemm_impl(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k,
+                      const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  int rc = check_gemm_args(fn, qtype, w, N, K, x_q8k, M);
   if (rc) return rc;
-  if (!y) return fail(DLLM_E_ARG, "dllm_qgemm: null output pointer");
-  if (ldy < N) return fail(DLLM_E_ARG, "dllm_qgemm: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
-  if (!aligned(y, 4) || !aligned(x_dmax, 4)) return fail(DLLM_E_ALIGN, "dllm_qgemm: y and x_dmax must be 4-byte aligned");
+  if (!y) return fail(DLLM_E_ARG, "%s: null output pointer", fn);
+  if (ldy < N) return fail(DLLM_E_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (!aligned(y, 4) || !aligned(x_dmax, 4) || !aligned(bias, 4))
+    return fail(DLLM_E_ALIGN, "%s: y, x_dmax and bias must be 4-byte aligned", fn);
   Plan pl = plan_gemm(qtype, N, K, M, true);
   const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
   if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
@@ -359,14 +364,29 @@ int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k
     p.out = y;
     p.ldo = ldy;
     p.split_stride = 0;
-    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), "dllm_qgemm launch"))) return rc;
+    p.bias = bias;
+    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn))) return rc;
     return ok();
   }
   p.out = (float*)workspace;
   p.ldo = N;
   p.split_stride = M * N;
-  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), "dllm_qgemm launch"))) return rc;
-  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, s), "dllm_qgemm reduce launch");
+  p.bias = nullptr;  // the reduction adds it once
+  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn))) return rc;
+  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, bias, s), fn);
+}
+
+int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax, int64_t M,
+               float* y, int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
+  return qgemm_impl("dllm_qgemm", qtype, w, N, K, x_q8k, x_dmax, M, nullptr, y, ldy, workspace, workspace_bytes,
+                    stream);
+}
+
+int dllm_qgemm_bias(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax,
+                    int64_t M, const float* bias, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
+  return qgemm_impl("dllm_qgemm_bias", qtype, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, workspace_bytes,
+                    stream);
 }
 
 static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -453,6 +473,7 @@ static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int6
   p.out = logits;
   p.keys = keys;
   p.stats = stats;
+  p.bias = nullptr;
   p.N = N;
   p.SB = SB;
   p.M = n_rows;

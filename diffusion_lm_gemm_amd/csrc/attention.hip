@@ -5,9 +5,10 @@
 // difference from autoregressive execution"; README, the GPU bullet: attention
 // on the f16 tensor cores with a softmax over the keys).
 //
-// One work-group per (64 queries, head), eight waves.  The head's K
-// (row-major) and V^T are converted to f16 into LDS once, all keys (L <= 256,
-// the canvas is about 100-160 tokens).  Wave w takes queries 16 (w & 3) ..
+// One work-group per (64 queries, query head), eight waves.  The K (row-major)
+// and V^T of its key/value head (the query head itself, or with grouped-query
+// attention head h / (H / Hkv)) are converted to f16 into LDS once, all keys
+// (L <= 256, the canvas is about 100-160 tokens).  Wave w takes queries 16 (w & 3) ..
 // +15 and one half of the 32-key chunks (w >> 2: the first ceil(C/2) chunks
 // or the rest), so two waves share each SIMD and each runs half the chain:
 //   S^T = K Q^T on v_mfma_f32_16x16x32_f16 (A = 16 keys from LDS, B = the
@@ -47,8 +48,8 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 // compiler can overlap LDS reads, MFMAs and the softmax across key blocks.
 template <int NKB>
 __global__ __launch_bounds__(64 * AT_NW) void k_attention(const float* __restrict__ qkv, int64_t L, int64_t ld,
-                                                        int64_t H, float* __restrict__ out, int64_t ldo,
-                                                        float scale) {
+                                                        int64_t H, int64_t Hkv, float* __restrict__ out,
+                                                        int64_t ldo, float scale) {
   static_assert(NKB % 2 == 0 && NKB >= 2 && NKB <= AT_KB, "whole 32-key chunks, at most AT_LMAX keys");
   __shared__ __attribute__((aligned(16))) _Float16 s_k[AT_LMAX * AT_KS];
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[AT_D * AT_VS];
@@ -56,10 +57,10 @@ __global__ __launch_bounds__(64 * AT_NW) void k_attention(const float* __restric
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qg = wv & (AT_QG - 1), kh = wv / AT_QG;
   const int r = lane & 15, g = lane >> 4;
-  const int64_t h = blockIdx.y;
+  const int64_t h = blockIdx.y, hkv = h / (H / Hkv);  // query head, its key/value head
   const int Lm1 = (int)L - 1;
-  const float* kbase = qkv + H * AT_D + h * AT_D;
-  const float* vbase = qkv + 2 * H * AT_D + h * AT_D;
+  const float* kbase = qkv + H * AT_D + hkv * AT_D;
+  const float* vbase = qkv + (H + Hkv) * AT_D + hkv * AT_D;
 
   // ---- the wave's queries (B operand of S^T: dims 32c + 8g .. +7 of query
   // q0 + r), loaded first so that their latency overlaps the staging
@@ -232,18 +233,18 @@ __global__ __launch_bounds__(64 * AT_NW) void k_attention(const float* __restric
 
 bool attention_fits(int64_t L, int64_t D) { return D == AT_D && L >= 1 && L <= AT_LMAX; }
 
-hipError_t launch_attention(const float* qkv, int64_t L, int64_t ld, int64_t H, float* out, int64_t ldo, float scale,
-                            hipStream_t s) {
+hipError_t launch_attention(const float* qkv, int64_t L, int64_t ld, int64_t H, int64_t Hkv, float* out, int64_t ldo,
+                            float scale, hipStream_t s) {
   const dim3 grid((unsigned)((L + AT_QW * AT_QG - 1) / (AT_QW * AT_QG)), (unsigned)H), block(64 * AT_NW);
   switch ((L + 31) / 32 * 2) {  // key blocks of 16 in whole 32-key chunks
-    case 2: hipLaunchKernelGGL((k_attention<2>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 4: hipLaunchKernelGGL((k_attention<4>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 6: hipLaunchKernelGGL((k_attention<6>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 8: hipLaunchKernelGGL((k_attention<8>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 10: hipLaunchKernelGGL((k_attention<10>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 12: hipLaunchKernelGGL((k_attention<12>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 14: hipLaunchKernelGGL((k_attention<14>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
-    case 16: hipLaunchKernelGGL((k_attention<16>), grid, block, 0, s, qkv, L, ld, H, out, ldo, scale); break;
+    case 2: hipLaunchKernelGGL((k_attention<2>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 4: hipLaunchKernelGGL((k_attention<4>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 6: hipLaunchKernelGGL((k_attention<6>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 8: hipLaunchKernelGGL((k_attention<8>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 10: hipLaunchKernelGGL((k_attention<10>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 12: hipLaunchKernelGGL((k_attention<12>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 14: hipLaunchKernelGGL((k_attention<14>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
+    case 16: hipLaunchKernelGGL((k_attention<16>), grid, block, 0, s, qkv, L, ld, H, Hkv, out, ldo, scale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

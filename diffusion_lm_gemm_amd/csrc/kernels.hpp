@@ -13,6 +13,7 @@ struct GemmParams {
   float* out;            // y (no split) or split partials
   uint64_t* keys;        // argmax keys [n_tiles][M] (LM head) or null
   float2* stats;         // with keys: softmax statistics (m, s) [n_tiles][M], or null
+  const float* bias;     // f32 [N] added to every output row (no split only), or null
   int64_t N, SB, M;
   int64_t ldo;           // leading dimension of out
   int64_t split_stride;  // floats between split slices of out
@@ -39,10 +40,11 @@ hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, i
                                        uint8_t* y, float* dmax, hipStream_t s);
 hipError_t launch_swiglu_quantize_q8k(const float* gu, int64_t ldgu, int64_t M, int64_t SB, uint8_t* y, float* dmax,
                                       hipStream_t s);
-// Bidirectional attention (attention.hip): head dimension 128, 1 <= L <= 256.
+// Bidirectional attention (attention.hip): head dimension 128, 1 <= L <= 256;
+// H query heads over Hkv key/value heads (Hkv divides H).
 bool attention_fits(int64_t L, int64_t D);
-hipError_t launch_attention(const float* qkv, int64_t L, int64_t ld, int64_t H, float* out, int64_t ldo, float scale,
-                            hipStream_t s);
+hipError_t launch_attention(const float* qkv, int64_t L, int64_t ld, int64_t H, int64_t Hkv, float* out, int64_t ldo,
+                            float scale, hipStream_t s);
 hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* out, hipStream_t s);
 // cfg: tile configuration (1: 64 rows, 4 waves x 16; 2: 128 rows, 8 waves x 16;
 // 3: 256 rows, 8 waves x 32, up to 80 tokens; 4: 128 rows, 4 waves x 32, up
@@ -53,7 +55,9 @@ hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* o
 int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
-hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s);
+// y = the sum of the S partial slices, plus bias[n] per column when bias is not null.
+hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
+                               hipStream_t s);
 bool lmhead_stream_fits(int64_t K, int64_t n_rows);
 int lmhead_stream_waves();             // the most waves (key slots per row) it uses
 int64_t lmhead_stream_slots(int64_t N);  // the waves it uses for N rows

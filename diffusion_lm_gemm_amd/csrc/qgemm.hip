@@ -545,15 +545,23 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   }
 
   // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
+  // (plus the bias of those rows, when given: only without a K split, whose
+  // reduction adds it instead)
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int64_t nbase = row0 + 16 * b + 4 * g4;
+    v4f bv = {0.f, 0.f, 0.f, 0.f};
+    if (p.bias) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nbase + i < N) bv[i] = p.bias[nbase + i];
+    }
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       const int64_t m = m0 + t * 16 + r;
       const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
-      const v4f yv = yacc[b][t] * inv;
+      const v4f yv = p.bias ? yacc[b][t] * inv + bv : yacc[b][t] * inv;
       yacc[b][t] = yv;
       if (m < M) {
         float* dst = outp + m * p.ldo + nbase;
@@ -626,11 +634,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 // zero.  SC > 0 fixes the number of slices at compile time, so that all of a
 // thread's loads are in flight together; SC == 0 takes S at run time, four
 // slices at a time.  VEC: the four elements are one 16-byte store (N and ldy
-// multiples of four, y 16-byte aligned); otherwise element stores, which
-// also handle a row change inside the four.
+// multiples of four, y and bias 16-byte aligned); otherwise element stores,
+// which also handle a row change inside the four.  A bias (f32 per column,
+// or null) is added to the sum once.
 template <int SC, bool VEC>
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int S, int64_t M,
-                                                    int64_t N, float* __restrict__ y, int64_t ldy) {
+                                                    int64_t N, float* __restrict__ y, int64_t ldy,
+                                                    const float* __restrict__ bias) {
   if constexpr (SC > 0) S = SC;
   const int64_t MN = M * N;
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -665,11 +675,12 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
   }
   int64_t m = e0 / N, n = e0 - m * N;
   if constexpr (VEC) {
+    if (bias) acc += *(const v4f*)(bias + n);
     *(v4f*)(y + m * ldy + n) = acc;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (e0 + i < MN) y[m * ldy + n] = acc[i];
+      if (e0 + i < MN) y[m * ldy + n] = bias ? acc[i] + bias[n] : acc[i];
       if (++n == N) { n = 0; ++m; }
     }
   }
@@ -822,24 +833,26 @@ hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 gr
 }
 
 template <bool VEC>
-static void launch_reduce_s(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
+static void launch_reduce_s(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
+                            hipStream_t s) {
   const dim3 grid((unsigned)((M * N + 1023) / 1024)), block(256);
   switch (S) {
-    case 2: hipLaunchKernelGGL((k_split_reduce<2, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
-    case 3: hipLaunchKernelGGL((k_split_reduce<3, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
-    case 4: hipLaunchKernelGGL((k_split_reduce<4, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
-    case 6: hipLaunchKernelGGL((k_split_reduce<6, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
-    case 8: hipLaunchKernelGGL((k_split_reduce<8, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
-    default: hipLaunchKernelGGL((k_split_reduce<0, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy); break;
+    case 2: hipLaunchKernelGGL((k_split_reduce<2, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
+    case 3: hipLaunchKernelGGL((k_split_reduce<3, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
+    case 4: hipLaunchKernelGGL((k_split_reduce<4, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
+    case 6: hipLaunchKernelGGL((k_split_reduce<6, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
+    case 8: hipLaunchKernelGGL((k_split_reduce<8, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
+    default: hipLaunchKernelGGL((k_split_reduce<0, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
   }
 }
 
-hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, hipStream_t s) {
-  const bool vec = (N % 4 == 0) && (ldy % 4 == 0) && ((((uintptr_t)y) & 15) == 0);
+hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
+                               hipStream_t s) {
+  const bool vec = (N % 4 == 0) && (ldy % 4 == 0) && ((((uintptr_t)y) & 15) == 0) && ((((uintptr_t)bias) & 15) == 0);
   if (vec)
-    launch_reduce_s<true>(ws, S, M, N, y, ldy, s);
+    launch_reduce_s<true>(ws, S, M, N, y, ldy, bias, s);
   else
-    launch_reduce_s<false>(ws, S, M, N, y, ldy, s);
+    launch_reduce_s<false>(ws, S, M, N, y, ldy, bias, s);
   return hipGetLastError();
 }
 

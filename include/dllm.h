@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 5
+#define DLLM_ABI_VERSION 6
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -107,21 +107,25 @@ int dllm_swiglu_quantize_q8k(const float *gu, int64_t M, int64_t F,
  * "Transformer Execution" and "Critical difference from autoregressive
  * execution": full, not causal, attention over the diffusion region; README,
  * the GPU bullet: attention on the f16 tensor cores with a softmax over the
- * keys).  Per head h and query i:
+ * keys).  Per query head h and query i:
  *   out[i][h D + d] = sum_j softmax_j(scale * q_i . k_j) v_jd
- * over all L keys, with q, k, v rounded to f16 (round to nearest even) and the
- * scores, softmax and sums in f32.
- *   qkv  f32 [L][ld_qkv]: per row Q (H*D values, head h at h*D), then K, then
- *        V -- the layout of one GEMM over the stacked Q, K, V weights
+ * over all L keys of key/value head h / (H / H_kv), with q, k, v rounded to
+ * f16 (round to nearest even) and the scores, softmax and sums in f32.
+ * H_kv = H is multi-head attention (LLaDA-8B); H_kv < H, dividing H, is
+ * grouped-query attention (Dream-7B, README milestones: "GQA").
+ *   qkv  f32 [L][ld_qkv]: per row Q (H heads of D values, head h at h*D),
+ *        then K (H_kv heads), then V (H_kv heads) -- the layout of one GEMM
+ *        over the stacked Q, K, V weights
  *   out  f32 [L][ld_out] (written: H*D values per row)
  *   scale  finite (1/sqrt(D) for standard attention)
  * D must be 128 and 1 <= L <= 256 (a head's keys stay in LDS): DLLM_E_SHAPE
- * otherwise.  qkv and out 16-byte aligned, ld_qkv >= 3*H*D and ld_out >= H*D
- * multiples of 4.  RoPE, if the model uses it, is applied to Q and K before.
+ * otherwise; H_kv must divide H.  qkv and out 16-byte aligned,
+ * ld_qkv >= (H + 2*H_kv)*D and ld_out >= H*D multiples of 4.  RoPE, if the
+ * model uses it, is applied to Q and K before.
  */
 int dllm_attention(const float *qkv, int64_t L, int64_t ld_qkv, int64_t H,
-                   int64_t D, float scale, float *out, int64_t ld_out,
-                   void *stream);
+                   int64_t H_kv, int64_t D, float scale, float *out,
+                   int64_t ld_out, void *stream);
 
 /*
  * Decode Q4_K / Q6_K super-blocks into the shared form both types reduce to
@@ -161,6 +165,19 @@ int dllm_qgemm(int qtype, const void *w, int64_t N, int64_t K,
                const void *x_q8k, const float *x_dmax, int64_t M, float *y,
                int64_t ldy, void *workspace, int64_t workspace_bytes,
                void *stream);
+
+/*
+ * dllm_qgemm plus a bias per output feature: y[m][n] = sum_k W_hat[n][k] *
+ * X_hat[m][k] + bias[n] (the Q, K and V projections of Dream-7B, README
+ * milestones: "QKV bias").  bias is f32 [N], 4-byte aligned, caller-owned;
+ * NULL gives exactly dllm_qgemm.  Without a K split the bias is added in the
+ * GEMM's epilogue, with one in the split reduction, once either way; the
+ * other arguments, the workspace rules and the errors are dllm_qgemm's.
+ */
+int dllm_qgemm_bias(int qtype, const void *w, int64_t N, int64_t K,
+                    const void *x_q8k, const float *x_dmax, int64_t M,
+                    const float *bias, float *y, int64_t ldy, void *workspace,
+                    int64_t workspace_bytes, void *stream);
 
 /*
  * Masked-row LM head (Development plan, "Compute design", last bullet; README

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -148,16 +148,37 @@ def test_fused_producer_argument_errors(dl):
 def test_attention_argument_errors(dl):
     L = dl.lib
     A = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never dereferenced
-    assert L.dllm_attention(A, 148, 3 * 4096, 32, 64, 0.1, A, 4096, None) == dl.E_SHAPE  # D != 128
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 32, 64, 0.1, A, 4096, None) == dl.E_SHAPE  # D != 128
     assert "128" in dl.last_error()
-    assert L.dllm_attention(A, 257, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE  # L > 256
-    assert L.dllm_attention(A, 0, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE
-    assert L.dllm_attention(A, 148, 3 * 4096 - 4, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
-    assert L.dllm_attention(A, 148, 3 * 4096, 32, 128, 0.1, A, 4092, None) == dl.E_ARG
-    assert L.dllm_attention(A, 148, 3 * 4096, 32, 128, float("inf"), A, 4096, None) == dl.E_ARG
-    assert L.dllm_attention(ctypes.c_void_p((1 << 20) + 4), 148, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_ALIGN
-    assert L.dllm_attention(A, 148, 3 * 4096 + 2, 32, 128, 0.1, A, 4096, None) == dl.E_ALIGN
-    assert L.dllm_attention(None, 148, 3 * 4096, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
+    assert L.dllm_attention(A, 257, 3 * 4096, 32, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE  # L > 256
+    assert L.dllm_attention(A, 0, 3 * 4096, 32, 32, 128, 0.1, A, 4096, None) == dl.E_SHAPE
+    assert L.dllm_attention(A, 148, 3 * 4096 - 4, 32, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 32, 128, 0.1, A, 4092, None) == dl.E_ARG
+    assert L.dllm_attention(A, 148, 3 * 4096, 32, 32, 128, float("inf"), A, 4096, None) == dl.E_ARG
+    assert L.dllm_attention(ctypes.c_void_p((1 << 20) + 4), 148, 3 * 4096, 32, 32, 128, 0.1, A, 4096,
+                            None) == dl.E_ALIGN
+    assert L.dllm_attention(A, 148, 3 * 4096 + 2, 32, 32, 128, 0.1, A, 4096, None) == dl.E_ALIGN
+    assert L.dllm_attention(None, 148, 3 * 4096, 32, 32, 128, 0.1, A, 4096, None) == dl.E_ARG
+    # grouped-query attention: H_kv must divide H; the row holds Q of H heads
+    # and K, V of H_kv heads (Dream-7B: 28 and 4, (28 + 8) * 128 = 4608)
+    assert L.dllm_attention(A, 148, 4608, 28, 5, 128, 0.1, A, 3584, None) == dl.E_SHAPE
+    assert "H_kv" in dl.last_error()
+    assert L.dllm_attention(A, 148, 4608, 28, 0, 128, 0.1, A, 3584, None) == dl.E_SHAPE
+    assert L.dllm_attention(A, 148, 4604, 28, 4, 128, 0.1, A, 3584, None) == dl.E_ARG
+    assert L.dllm_attention(A, 148, 4608, 28, 4, 128, 0.1, A, 3580, None) == dl.E_ARG
+
+
+def test_qgemm_bias_argument_errors(dl):
+    L = dl.lib
+    FAKE = ctypes.c_void_p(1 << 20)
+    # a bias must be 4-byte aligned; the rest are dllm_qgemm's checks
+    assert L.dllm_qgemm_bias(dl.Q4_K, FAKE, 64, 256, FAKE, None, 4, ctypes.c_void_p((1 << 20) + 2), FAKE, 64,
+                             None, 0, None) == dl.E_ALIGN
+    assert "bias" in dl.last_error()
+    assert L.dllm_qgemm_bias(dl.Q4_K, FAKE, 64, 300, FAKE, None, 4, FAKE, FAKE, 64, None, 0, None) == dl.E_SHAPE
+    assert L.dllm_qgemm_bias(8, FAKE, 64, 256, FAKE, None, 4, FAKE, FAKE, 64, None, 0, None) == dl.E_UNSUPPORTED
+    assert L.dllm_qgemm_bias(dl.Q6_K, FAKE, 64, 256, FAKE, None, 4, FAKE, None, 64, None, 0, None) == dl.E_ARG
+    assert "dllm_qgemm_bias" in dl.last_error()
 
 
 def test_workspace_queries(dl):
