@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--L", type=int, default=148, help="canvas tokens")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dream", action="store_true", help="skip the Dream-7B-shaped step (a reported extra)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--profile-dominant", action="store_true",
                     help="for hardware-counter runs: a 256 MiB device copy (the counters' calibration), then "
@@ -51,6 +52,104 @@ def parse():
 
 
 DOMINANT = ("qgemm_q4k", 2 * FFN, D)  # gate/up: the call that takes most of the step
+
+
+# Dream-7B's layer dimensions (the model's published configuration; the pages
+# name the model, its GQA, QKV bias and 152 064-column output projection)
+DREAM = {"D": 3584, "FFN": 18944, "HQ": 28, "HKV": 4, "HD": 128, "LAYERS": 28, "VOCAB": 152064}
+
+
+def dream_step(dl, synth, torch, dev, L, seed, graph_node_ms):
+    """The same step for Dream-7B's shapes (a reported extra, not `value`):
+    28 layers of Q+K+V (with their bias; V in Q6_K in even layers), O, gate+up
+    and down (Q6_K in even layers), each after a quantize, then the LM head
+    over every masked position (the 128 generated rows, logits from the row
+    before each).  Captured as one graph, the median of 5 replays; also the
+    grouped-query attention of one layer.  Weights are freed afterwards."""
+    Q4, Q6 = dl.Q4_K, dl.Q6_K
+    D, FFN, HQ, HKV, HD, NL, VOC = (DREAM[k] for k in ("D", "FFN", "HQ", "HKV", "HD", "LAYERS", "VOCAB"))
+    NQKV = (HQ + 2 * HKV) * HD
+    masked = L - 20
+    lay = []
+    for l in range(NL):
+        even = l % 2 == 0
+        lw = {"even": even, "bias": synth.normal_f32((NQKV,), seed, f"D{l:02d}.qkv_bias", dev)}
+        if even:
+            lw["qk"] = synth.q4k_rows(NQKV - HKV * HD, D, seed, f"D{l:02d}.attn_qk", dev)
+            lw["v"] = synth.q6k_rows(HKV * HD, D, seed, f"D{l:02d}.attn_v", dev)
+            lw["down"] = synth.q6k_rows(D, FFN, seed, f"D{l:02d}.ffn_down", dev)
+        else:
+            lw["qkv"] = synth.q4k_rows(NQKV, D, seed, f"D{l:02d}.attn_qkv", dev)
+            lw["down"] = synth.q4k_rows(D, FFN, seed, f"D{l:02d}.ffn_down", dev)
+        lw["o"] = synth.q4k_rows(D, D, seed, f"D{l:02d}.attn_output", dev)
+        lw["gu"] = synth.q4k_rows(2 * FFN, D, seed, f"D{l:02d}.ffn_gate_up", dev)
+        lay.append(lw)
+    x_d = synth.normal_f32((L, D), seed, "D.x", dev)
+    x_f = synth.normal_f32((L, FFN), seed, "D.act", dev)
+    w_out = synth.q6k_rows(VOC, D, seed, "D.output", dev)
+    hidden = synth.normal_f32((L, D), seed, "D.hidden", dev)
+    rows = torch.arange(19, 19 + masked, dtype=torch.int32, device=dev)
+    xq_d = torch.empty((L, D // 256 * 292), dtype=torch.uint8, device=dev)
+    xq_f = torch.empty((L, FFN // 256 * 292), dtype=torch.uint8, device=dev)
+    dm_d = torch.empty(L, dtype=torch.float32, device=dev)
+    dm_f = torch.empty(L, dtype=torch.float32, device=dev)
+    y_qkv = torch.empty((L, NQKV), dtype=torch.float32, device=dev)
+    y_o = torch.empty((L, D), dtype=torch.float32, device=dev)
+    y_gu = torch.empty((L, 2 * FFN), dtype=torch.float32, device=dev)
+    y_dn = torch.empty((L, D), dtype=torch.float32, device=dev)
+    logits = torch.empty((masked, VOC), dtype=torch.float32, device=dev)
+    amax = torch.empty(masked, dtype=torch.int32, device=dev)
+    shapes = [(Q4, NQKV - HKV * HD, D), (Q6, HKV * HD, D), (Q4, NQKV, D), (Q4, D, D), (Q4, 2 * FFN, D),
+              (Q4, D, FFN), (Q6, D, FFN)]
+    ws = torch.zeros(max(256, max(dl.qgemm_workspace_bytes(q, n, k, L) for q, n, k in shapes)),
+                     dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(dl.lmhead_workspace_bytes(Q6, VOC, D, masked), dtype=torch.uint8, device=dev)
+    fns, byts, ops = [], 0, 0
+
+    def quant(x, out, dm):
+        nonlocal byts
+        fns.append(lambda: dl.quantize_q8k(x, out, dm))
+        byts += x.numel() * 4 + x.numel() // 256 * 292
+
+    def gemm(q, w, N, K, xq, dm, y, bias=None):
+        nonlocal byts, ops
+        fns.append(lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws, x_dmax=dm, bias=bias))
+        byts += N * K // 256 * dl.block_bytes(q) + L * K // 256 * 292 + L * N * 4
+        ops += 2 * L * N * K
+
+    for lw in lay:
+        quant(x_d, xq_d, dm_d)
+        if lw["even"]:
+            nqk = NQKV - HKV * HD
+            gemm(Q4, lw["qk"], nqk, D, xq_d, dm_d, y_qkv[:, :nqk], lw["bias"][:nqk])
+            gemm(Q6, lw["v"], HKV * HD, D, xq_d, dm_d, y_qkv[:, nqk:], lw["bias"][nqk:])
+        else:
+            gemm(Q4, lw["qkv"], NQKV, D, xq_d, dm_d, y_qkv, lw["bias"])
+        quant(x_d, xq_d, dm_d)
+        gemm(Q4, lw["o"], D, D, xq_d, dm_d, y_o)
+        quant(x_d, xq_d, dm_d)
+        gemm(Q4, lw["gu"], 2 * FFN, D, xq_d, dm_d, y_gu)
+        quant(x_f, xq_f, dm_f)
+        gemm(Q6 if lw["even"] else Q4, lw["down"], D, FFN, xq_f, dm_f, y_dn)
+    fns.append(lambda: dl.lmhead_masked(Q6, w_out, VOC, D, hidden, rows, logits, amax, ws_lm))
+    byts += masked * D * 4 + masked * D // 256 * 292 + VOC * D // 256 * dl.block_bytes(Q6) + masked * VOC * 4
+    ops += 2 * masked * VOC * D
+    step_ms = graph_node_ms(fns) * len(fns)
+    attn_out = torch.empty((L, HQ * HD), dtype=torch.float32, device=dev)
+    a_ms = graph_node_ms([lambda: dl.attention(y_qkv, HQ, HD, None, attn_out, H_kv=HKV)] * 20)
+    out = {"ms_per_step": round(step_ms, 4), "int8_TOPS": round(ops / (step_ms * 1e-3) / 1e12, 2),
+           "GBps": round(byts / (step_ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(byts / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "calls_per_step": len(fns), "step_algorithmic_bytes": byts,
+           "attention_gqa": {"avg_ms": round(a_ms, 5), "shape": f"L={L}, {HQ} query / {HKV} key-value heads x {HD}",
+                             "in_step": False},
+           "workload": f"Dream-7B Q4_K_M shapes, L={L}: {NL} layers (Q+K+V {NQKV}x{D} with bias, O {D}x{D}, "
+                       f"gate+up {2 * FFN}x{D}, down {D}x{FFN}; attn_v/ffn_down Q6_K in even layers) + LM head "
+                       f"{masked}x{VOC}x{D} Q6_K over every masked row",
+           "timing": "one graph of the step's calls, median of 5 replays"}
+    del lay, w_out
+    torch.cuda.empty_cache()
+    return out
 
 
 def profile_dominant(args):
@@ -320,6 +419,9 @@ def main():
     attention = {"avg_ms": round(a_ms, 5), "TFLOPs": round(a_flops / (a_ms * 1e-3) / 1e12, 2),
                  "GBps": round((L * 3 * D * 4 + L * D * 4) / (a_ms * 1e-3) / 1e9, 1),
                  "shape": f"L={L}, 32 heads x 128, f16 operands", "in_step": False}
+    dream = None if args.no_dream else dream_step(dl, synth, torch, dev, L, seed, graph_node_ms)
+    if dream:
+        print(f"[bench] dream-7B step: {dream['ms_per_step']} ms", file=sys.stderr, flush=True)
     print(f"[bench] per-call kinds: " + json.dumps(kinds), file=sys.stderr, flush=True)
     print(f"[bench] per-call shapes: " + json.dumps(shapes), file=sys.stderr, flush=True)
 
@@ -381,6 +483,7 @@ def main():
                               "in_step": False},
         "fused_producers": dict(fused_out, in_step=False),
         "attention": attention,
+        "dream_step": dream,
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),
     }
