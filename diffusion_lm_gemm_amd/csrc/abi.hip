@@ -113,7 +113,8 @@ constexpr double kCfgQ6Factor[8] = {0.0, 0.873, 1.173, 1.864, 2.002, 1.039, 1.6,
 
 // Measured best (tile configuration, K split) for the linear layers of the
 // LLaDA-8B step (d = 4096, FFN 12288; Q4_K, and Q6_K for attn_v / ffn_down)
-// at canvases of 129..160 tokens, from timing every candidate on MI355X.
+// and of Dream-7B (d = 3584, FFN 18944) at canvases of 129..160 tokens, from
+// timing every candidate on MI355X (at 148 tokens, weights streamed from HBM).
 // Shapes not listed go to the cost model below.
 struct Tuned {
   int qtype;
@@ -128,6 +129,14 @@ constexpr Tuned kTuned[] = {
     {14, 4096, 4096, 129, 160, 5, 4},   // V
     {12, 4096, 12288, 129, 160, 6, 4},  // down
     {14, 4096, 12288, 129, 160, 5, 8},  // down
+    // Dream-7B (hidden 3584, 4 key/value heads of 128, FFN 18944)
+    {12, 4608, 3584, 129, 160, 6, 1},    // Q + K + V
+    {12, 4096, 3584, 129, 160, 6, 2},    // Q + K (V in Q6_K)
+    {14, 512, 3584, 129, 160, 6, 14},    // V
+    {12, 3584, 3584, 129, 160, 6, 2},    // O
+    {12, 37888, 3584, 129, 160, 7, 1},   // gate + up
+    {12, 3584, 18944, 129, 160, 7, 6},   // down
+    {14, 3584, 18944, 129, 160, 2, 9},   // down
 };
 
 // DLLM_QGEMM_PLAN="qtype:N:K:cfg:S,..." replaces (or adds) tuned entries for
