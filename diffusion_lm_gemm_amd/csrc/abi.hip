@@ -492,7 +492,7 @@ static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int6
   const int tb = tb_for(n_rows);
   const int64_t n_tiles = cdiv(N, 64);  // 4 waves, 64 rows per work-group
   const dim3 grid((unsigned)n_tiles, 1, (unsigned)cdiv(n_rows, 16 * tb));
-  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 1, grid, true, s), "lm head gemm launch"))) return rc;
+  if ((rc = hip_status(launch_qgemm(qtype, p, tb, 5, grid, true, s), "lm head gemm launch"))) return rc;
   return hip_status(launch_argmax_finalize(keys, stats, n_tiles, n_rows, argmax, lse, p_max, s), "lm head argmax launch");
 }
 

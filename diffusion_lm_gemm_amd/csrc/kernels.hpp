@@ -51,7 +51,7 @@ hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* o
 // to 80 tokens; 5: 64 rows, 4 waves x 16, one activation stage, two
 // work-groups per CU; 6: 64 rows, 4 waves x 16, up to 80 tokens, two
 // work-groups per CU; 7: 192 rows, 12 waves x 16, up to 80 tokens).  argmax
-// forces cfg 1.
+// forces cfg 5.
 int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);

@@ -580,16 +580,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     // per token: best (value, lowest row index) over this work-group's rows
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
+      // every key is formed and rows past N select 0 (no branch per element)
       uint64_t best = 0;
 #pragma unroll
       for (int b = 0; b < RB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t n = row0 + 16 * b + 4 * g4 + i;
-          if (n < N) {
-            const uint64_t key = ((uint64_t)f32_order_bits(yacc[b][t][i]) << 32) | (uint64_t)(~(uint32_t)n);
-            best = key > best ? key : best;
-          }
+          const uint64_t key = ((uint64_t)f32_order_bits(yacc[b][t][i]) << 32) | (uint64_t)(~(uint32_t)n);
+          const uint64_t kv = n < N ? key : 0ull;
+          best = kv > best ? kv : best;
         }
       const uint64_t o1 = __shfl_xor(best, 16);
       best = o1 > best ? o1 : best;
@@ -796,10 +796,12 @@ static hipError_t launch_q(const GemmParams& p, int tb, dim3 grid, hipStream_t s
 //   cfg 6: 4 x 1 (64 rows), up to 80 tokens, two work-groups per CU (the
 //          cfg 1 kernel on at most five token blocks)
 //   cfg 7: 12 x 1 (192 rows), up to 80 tokens (three waves per SIMD)
-// The LM head (argmax) uses cfg 1.
+// The LM head (argmax) uses cfg 5: the same 64-row tiles as cfg 1, whose
+// plain GEMM it outruns at the LM head's shapes (one activation stage, two
+// work-groups per CU).
 template <int QT>
 static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
-  if (argmax) return launch_q<QT, 4, 1, true>(p, tb, grid, s);
+  if (argmax) return launch_q<QT, 4, 1, true, 1>(p, tb, grid, s);
   if (cfg == 1 || cfg == 6) return launch_q<QT, 4, 1, false>(p, tb, grid, s);
   if (cfg == 2) return launch_q<QT, 8, 1, false>(p, tb, grid, s);
   if (cfg == 5) return launch_q<QT, 4, 1, false, 1>(p, tb, grid, s);
