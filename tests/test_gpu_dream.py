@@ -149,3 +149,45 @@ def test_dream_lmhead_every_masked_row(dl):
     _check_argmax(lg, am, ref, ref_am, "dream lmhead")
     _check_confidence(lg, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
                       "dream lmhead confidence")
+
+
+def test_dream_lmhead_block_of_32_streams(dl, monkeypatch):
+    """A block of 32 masked rows at Dream's head takes the streaming kernel
+    (K = 3584 is 14 super-blocks, 152 064 rows): whole logits, argmax and
+    confidence against the oracle, and the tiled path on the same rows."""
+    N, K = VOCAB, D_MODEL
+    rows = torch.arange(60, 92, dtype=torch.int32)
+    w = _weights(14, N, K, 86, "dream-output-32")
+    h = synth.normal_f32((L, K), 86, "dream-hidden-32")
+    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
+    wd, hd, rd = w.to(DEV), h.to(DEV), rows.to(DEV)
+    lg, am, lse, p = dl.lmhead_confidence(14, wd, N, K, hd, rd)
+    lg = lg.cpu().numpy(); am = am.cpu().numpy()
+    assert_close_rows(lg, ref, "dream lmhead 32 rows")
+    _check_argmax(lg, am, ref, ref_am, "dream lmhead 32 rows")
+    _check_confidence(lg, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
+                      "dream lmhead 32 rows confidence")
+    monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
+    lg_t, am_t = dl.lmhead_masked(14, wd, N, K, hd, rd)
+    lg_t = lg_t.cpu().numpy(); am_t = am_t.cpu().numpy()
+    assert_close_rows(lg_t, ref, "dream lmhead 32 rows, tiled path")
+    _check_argmax(lg_t, am_t, ref, ref_am, "dream lmhead 32 rows, tiled path")
+
+
+def test_qgemm_bias_single_token_tile(dl):
+    """Fewer tokens than one 16-token tile (M = 5), Q4_K and Q6_K, with the K
+    split and without: the bias of every row, nothing on the padded tokens."""
+    for qtype in (12, 14):
+        N, K, M = 200, 3584, 5
+        w = _weights(qtype, N, K, 87, f"bias-small-{qtype}")
+        xq = oracle.quantize_q8k(synth.normal_f32((M, K), 87, "bias-small-x").numpy())
+        bias = synth.normal_f32((N,), 87, "bias-small-b")
+        ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M, bias=bias.numpy())
+        ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
+        for workspace in (ws, None):
+            big = torch.full((M + 3, N), 9.0, device=DEV)
+            dl.qgemm(qtype, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, y=big[:M], workspace=workspace,
+                     bias=bias.to(DEV))
+            got = big.cpu().numpy()
+            assert_close_rows(got[:M], ref, f"bias M=5 qtype={qtype} ws={workspace is not None}")
+            assert np.all(got[M:] == 9.0)
