@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
         if (m < M) {
           float* dst = p.logits + m * p.ldl + nbase;
           if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
-            *(v4f*)dst = yv;
+            __builtin_nontemporal_store(yv, (v4f*)dst);  // streamed out: its readers sit on other XCDs
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)

@@ -566,7 +566,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       if (m < M) {
         float* dst = outp + m * p.ldo + nbase;
         if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
-          *(v4f*)dst = yv;
+          // streamed out (non-temporal): the readers of y or of the split
+          // partials run on other XCDs and read them from memory anyway, and
+          // no dirty lines are left in this XCD's L2 for the kernel's end
+          __builtin_nontemporal_store(yv, (v4f*)dst);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
   int64_t m = e0 / N, n = e0 - m * N;
   if constexpr (VEC) {
     if (bias) acc += *(const v4f*)(bias + n);
-    *(v4f*)(y + m * ldy + n) = acc;
+    __builtin_nontemporal_store(acc, (v4f*)(y + m * ldy + n));  // streamed out, as the GEMM's own stores
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
