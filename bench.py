@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--profile-dominant", action="store_true",
                     help="for hardware-counter runs: a 256 MiB device copy (the counters' calibration), then "
                          "--steps launches of the step's dominant GEMM (one layer's gate/up), then exit")
+    ap.add_argument("--profile-kernel", choices=("lmhead", "attention"), default=None,
+                    help="for hardware-counter runs: the same calibration copy, then --steps launches of the masked-row "
+                         "LM head (32 rows x 126464 x 4096, Q6_K) or of attention (L tokens, 32 heads x 128), then exit")
     return ap.parse_args()
 
 
@@ -179,6 +182,41 @@ def profile_dominant(args):
           flush=True)
 
 
+def profile_kernel(args):
+    """The calibration copy of profile_dominant, then --steps launches of one
+    other call of the path: the masked-row LM head or bidirectional attention,
+    on inputs of the step's shapes."""
+    import torch
+    import diffusion_lm_gemm_amd as dl
+    import synth
+    dev = torch.device("cuda:0")
+    a = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    L = args.L
+    if args.profile_kernel == "lmhead":
+        w = synth.q6k_rows(VOCAB, D, args.seed, "output", dev)
+        hidden = synth.normal_f32((L, D), args.seed, "hidden", dev)
+        rows = torch.arange(20, 20 + MASKED, dtype=torch.int32, device=dev)
+        logits = torch.empty((MASKED, VOCAB), dtype=torch.float32, device=dev)
+        amax = torch.empty(MASKED, dtype=torch.int32, device=dev)
+        ws = torch.empty(dl.lmhead_workspace_bytes(dl.Q6_K, VOCAB, D, MASKED), dtype=torch.uint8, device=dev)
+        fn = lambda: dl.lmhead_masked(dl.Q6_K, w, VOCAB, D, hidden, rows, logits, amax, ws)
+        what = f"lmhead_masked Q6_K N={VOCAB} K={D} rows={MASKED} of M={L}"
+    else:
+        qkv = synth.normal_f32((L, 3 * D), args.seed, "qkv", dev)
+        out = torch.empty((L, D), dtype=torch.float32, device=dev)
+        fn = lambda: dl.attention(qkv, 32, 128, None, out)
+        what = f"attention L={L} H=32 D=128"
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"[profile-kernel] copy of {a.numel() * 4} bytes, then {args.steps} x {what}", flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,6 +228,9 @@ def main():
 
     if args.profile_dominant:
         profile_dominant(args)
+        return
+    if args.profile_kernel:
+        profile_kernel(args)
         return
 
     import torch
