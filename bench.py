@@ -48,9 +48,10 @@ def parse():
     ap.add_argument("--profile-dominant", action="store_true",
                     help="for hardware-counter runs: a 256 MiB device copy (the counters' calibration), then "
                          "--steps launches of the step's dominant GEMM (one layer's gate/up), then exit")
-    ap.add_argument("--profile-kernel", choices=("lmhead", "attention"), default=None,
+    ap.add_argument("--profile-kernel", choices=("lmhead", "attention", "rmsnorm", "swiglu"), default=None,
                     help="for hardware-counter runs: the same calibration copy, then --steps launches of the masked-row "
-                         "LM head (32 rows x 126464 x 4096, Q6_K) or of attention (L tokens, 32 heads x 128), then exit")
+                         "LM head (32 rows x 126464 x 4096, Q6_K), of attention (L tokens, 32 heads x 128) or of a fused "
+                         "producer (RMSNorm -> Q8_K over 4096 values, SwiGLU -> Q8_K over 2 x 12288), then exit")
     return ap.parse_args()
 
 
@@ -205,11 +206,24 @@ def profile_kernel(args):
         ws = torch.empty(dl.lmhead_workspace_bytes(dl.Q6_K, VOCAB, D, MASKED), dtype=torch.uint8, device=dev)
         fn = lambda: dl.lmhead_masked(dl.Q6_K, w, VOCAB, D, hidden, rows, logits, amax, ws)
         what = f"lmhead_masked Q6_K N={VOCAB} K={D} rows={MASKED} of M={L}"
-    else:
+    elif args.profile_kernel == "attention":
         qkv = synth.normal_f32((L, 3 * D), args.seed, "qkv", dev)
         out = torch.empty((L, D), dtype=torch.float32, device=dev)
         fn = lambda: dl.attention(qkv, 32, 128, None, out)
         what = f"attention L={L} H=32 D=128"
+    elif args.profile_kernel == "rmsnorm":
+        x = synth.normal_f32((L, D), args.seed, "x_norm", dev)
+        g = synth.normal_f32((D,), args.seed, "norm_weight", dev)
+        xq = torch.empty((L, D // 256 * 292), dtype=torch.uint8, device=dev)
+        dm = torch.empty(L, dtype=torch.float32, device=dev)
+        fn = lambda: dl.rmsnorm_quantize_q8k(x, g, 1e-5, xq, dm)
+        what = f"rmsnorm_quantize_q8k M={L} K={D}"
+    else:
+        gu = synth.normal_f32((L, 2 * FFN), args.seed, "gate_up", dev)
+        xq = torch.empty((L, FFN // 256 * 292), dtype=torch.uint8, device=dev)
+        dm = torch.empty(L, dtype=torch.float32, device=dev)
+        fn = lambda: dl.swiglu_quantize_q8k(gu, xq, dm)
+        what = f"swiglu_quantize_q8k M={L} F={FFN}"
     torch.cuda.synchronize()
     for _ in range(args.steps):
         fn()
