@@ -137,3 +137,21 @@ def test_gqa_group_mapping():
     got = oracle.attention(q2, H, D, 0.5, Hkv=Hkv).reshape(L, H, D)
     changed = [h for h in range(H) if not np.array_equal(got[:, h], base[:, h])]
     assert changed == list(range(G, 2 * G))
+
+
+def test_attention_against_torch_sdpa():
+    """torch's own scaled-dot-product attention (CPU, f64, no mask, its
+    grouped-query mode) on the same f16-rounded operands: an implementation
+    written apart from the oracle, with the same grouping of query heads."""
+    import torch
+    rng = np.random.default_rng(68)
+    for L, H, Hkv, D in ((9, 4, 4, 16), (23, 6, 2, 32), (31, 7, 1, 16)):
+        qkv = (rng.standard_normal((L, (H + 2 * Hkv) * D)) * 1.5).astype(np.float32)
+        r = torch.from_numpy(qkv.astype(np.float16).astype(np.float64))
+        q = r[:, :H * D].reshape(L, H, D).permute(1, 0, 2).unsqueeze(0)
+        k = r[:, H * D:(H + Hkv) * D].reshape(L, Hkv, D).permute(1, 0, 2).unsqueeze(0)
+        v = r[:, (H + Hkv) * D:].reshape(L, Hkv, D).permute(1, 0, 2).unsqueeze(0)
+        want = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=D ** -0.5, enable_gqa=True)
+        want = want.squeeze(0).permute(1, 0, 2).reshape(L, H * D).numpy()
+        got = oracle.attention(qkv, H, D, D ** -0.5, Hkv=Hkv)
+        assert np.allclose(got, want, rtol=1e-11, atol=1e-12)
