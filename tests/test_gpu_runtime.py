@@ -2,7 +2,8 @@
 and replayed (the bench's launch mode) give the eager results bit for bit on
 every replay, with unrelated eager work between replays; and calls on two
 streams at once, each with its own workspace, give the sequential results
-(the library keeps no state between calls)."""
+(the library keeps no state between calls); and the LM head writes through a
+row-strided logits view without touching the padding."""
 import numpy as np
 import pytest
 import torch
@@ -113,3 +114,22 @@ def test_two_streams_at_once_match_sequential(dl):
     torch.cuda.synchronize()
     for i in range(2):
         assert torch.equal(outs[i][0], seq[i][0]) and torch.equal(outs[i][1], seq[i][1]), f"stream {i}"
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_lmhead_strided_logits(dl, monkeypatch, tiled):
+    """Logits written through a row-strided view (ldl > N) equal the
+    contiguous call's, and the padding between rows is left alone, on the
+    streaming and the tiled path."""
+    if tiled:
+        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
+    N, K, L = 3000, 1024, 60
+    w = _weights(14, N, K, 94, "rt-lm").to(DEV)
+    h = synth.normal_f32((L, K), 94, "rt-lm-h").to(DEV)
+    rows = torch.tensor([3, 59, 0, 17, 42], dtype=torch.int32, device=DEV)
+    ref_lg, ref_am = dl.lmhead_masked(14, w, N, K, h, rows)
+    big = torch.full((rows.numel(), N + 12), -7.0, device=DEV)
+    lg, am = dl.lmhead_masked(14, w, N, K, h, rows, logits=big[:, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, :N], ref_lg) and torch.equal(am, ref_am)
+    assert torch.all(big[:, N:] == -7.0)
