@@ -32,7 +32,11 @@ HEADER_EXPORTS = (
     "dllm_swiglu_quantize_q8k", "dllm_attention", "dllm_decode_qk",
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_qgemm_bias", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
+    "dllm_qgemm_superblock_sums_i32", "dllm_qgemm_planned", "dllm_lmhead_planned",
 )
+
+# tile configurations of dllm_qgemm_planned and the super-block sums export
+TILE_CONFIGS = (1, 2, 3, 4, 5, 6, 7)
 
 
 class DllmError(RuntimeError):
@@ -62,6 +66,9 @@ def _load():
         "dllm_lmhead_masked": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, I64, P]),
         "dllm_lmhead_confidence": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, P]),
         "dllm_qgemm_partials_i32": (I, [I, P, I64, I64, P, I64, P, P]),
+        "dllm_qgemm_superblock_sums_i32": (I, [I, P, I64, I64, P, I64, P, I, I, P]),
+        "dllm_qgemm_planned": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P, I64, I, I, P]),
+        "dllm_lmhead_planned": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -282,3 +289,53 @@ def qgemm_partials_i32(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch
     P = torch.empty((M, N, K // QK_K, 16), dtype=torch.int32, device=dev)
     _check(lib.dllm_qgemm_partials_i32(qtype, _ptr(w), N, K, _ptr(x_q8k), M, _ptr(P), _stream(dev)))
     return P
+
+
+def qgemm_superblock_sums_i32(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor,
+                              M: int, tile: int, split: int = 1) -> torch.Tensor:
+    """Test export: int32 [M, N, K/256], the exact integer super-block sums
+    formed by the GEMM kernel of tile configuration `tile` (TILE_CONFIGS)
+    with K split `split`."""
+    dev = _dev(w)
+    A = torch.empty((M, N, K // QK_K), dtype=torch.int32, device=dev)
+    _check(lib.dllm_qgemm_superblock_sums_i32(qtype, _ptr(w), N, K, _ptr(x_q8k), M, _ptr(A), tile, split,
+                                              _stream(dev)))
+    return A
+
+
+def qgemm_planned(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: int,
+                  tile: int, split: int = 1, y: torch.Tensor | None = None,
+                  x_dmax: torch.Tensor | None = None, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """Test entry: qgemm with an explicit tile configuration (TILE_CONFIGS)
+    and K split; allocates the split's workspace."""
+    dev = _dev(w)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    assert y.dtype == torch.float32 and y.stride(1) == 1
+    ws = torch.empty(max(split * M * N * 4, 256), dtype=torch.uint8, device=dev)
+    _check(lib.dllm_qgemm_planned(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(bias), _ptr(y),
+                                  y.stride(0), _ptr(ws), ws.numel(), tile, split, _stream(dev)))
+    return y
+
+
+def lmhead_planned(qtype: int, w: torch.Tensor, N: int, K: int, h: torch.Tensor, rows: torch.Tensor,
+                   path: int, confidence: bool = True, logits: torch.Tensor | None = None):
+    """Test entry: the LM head on a given path (0 choose, 1 streaming, 2
+    tiled): (logits, argmax, lse, p_argmax), the last two None without
+    `confidence`.  `logits` (f32 [n_rows, >= N] rows, unit column stride) may
+    be given."""
+    dev = _dev(w)
+    assert h.dtype == torch.float32 and h.stride(1) == 1 and rows.dtype == torch.int32
+    M = h.shape[0]
+    n = rows.numel()
+    if logits is None:
+        logits = torch.empty((n, N), dtype=torch.float32, device=dev)
+    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    argmax = torch.empty(n, dtype=torch.int32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if confidence else None
+    p_am = torch.empty(n, dtype=torch.float32, device=dev) if confidence else None
+    workspace = torch.empty(max(lmhead_workspace_bytes(qtype, N, K, n), 1), dtype=torch.uint8, device=dev)
+    _check(lib.dllm_lmhead_planned(qtype, _ptr(w), N, K, _ptr(h), M, h.stride(0), _ptr(rows), n,
+                                   _ptr(logits), logits.stride(0), _ptr(argmax), _ptr(lse), _ptr(p_am),
+                                   _ptr(workspace), workspace.numel(), path, _stream(dev)))
+    return logits, argmax, lse, p_am

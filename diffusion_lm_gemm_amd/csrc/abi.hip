@@ -98,12 +98,22 @@ int tb_for(int64_t M) {
 constexpr int64_t kCUs = 256;  // MI355X compute units
 
 struct Plan {
-  int tb;
+  int tb;   // token blocks of 16 per work-group
   int cfg;  // tile configuration (rows per work-group: qgemm_cfg_rows(cfg))
   int64_t n_tiles, m_tiles;
   int S;    // K splits
   int sps;  // super-blocks per split
 };
+
+// The plan of a given configuration and K split (S is reduced to the
+// number of non-empty splits).
+Plan make_plan(int cfg, int S, int64_t N, int64_t K, int64_t M) {
+  const int64_t SB = K / 256;
+  const int64_t sps = cdiv(SB, S);
+  const int max_tb = qgemm_cfg_max_tb(cfg);
+  const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
+  return Plan{tb, cfg, cdiv(N, qgemm_cfg_rows(cfg)), cdiv(M, (int64_t)16 * tb), (int)cdiv(SB, sps), (int)sps};
+}
 
 // Time of one super-block step of a work-group with a full token tile, per
 // tile configuration, in microseconds, and its factor for Q6_K (heavier
@@ -139,37 +149,6 @@ constexpr Tuned kTuned[] = {
     {14, 3584, 18944, 129, 160, 2, 9},   // down
 };
 
-// DLLM_QGEMM_PLAN="qtype:N:K:cfg:S,..." replaces (or adds) tuned entries for
-// the listed shapes at any token count (for measuring alternatives in place).
-struct PlanOverride {
-  int qtype;
-  int64_t N, K;
-  int cfg, S;
-};
-static int plan_overrides(PlanOverride* out, int max_n) {
-  const char* e = getenv("DLLM_QGEMM_PLAN");
-  int n = 0;
-  while (e && *e && n < max_n) {
-    PlanOverride o;
-    long long q, nn, kk, c, s;
-    int used = 0;
-    if (sscanf(e, "%lld:%lld:%lld:%lld:%lld%n", &q, &nn, &kk, &c, &s, &used) != 5) break;
-    o.qtype = (int)q; o.N = nn; o.K = kk; o.cfg = (int)c; o.S = (int)s;
-    if (o.cfg >= 1 && o.cfg <= 7 && o.S >= 1 && o.S <= 16) out[n++] = o;
-    e += used;
-    if (*e == ',') ++e;
-  }
-  return n;
-}
-
-// DLLM_QGEMM_TILE=1..7 pins the tile configuration (for testing every
-// configuration on any shape); unset, the planner chooses.
-static int forced_cfg() {
-  const char* e = getenv("DLLM_QGEMM_TILE");
-  if (!e || e[0] < '1' || e[0] > '7' || e[1]) return -1;
-  return e[0] - '0';
-}
-
 // Pick the tile configuration and the K split that minimise an estimate of
 // the makespan: work-group rounds over the CUs times super-blocks per
 // work-group times the step time, plus, for a split, the reduction (~2.4 us
@@ -178,59 +157,66 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   Plan best{};
   double best_cost = 1e300;
   const int64_t SB = K / 256;
-  const int fc = forced_cfg();
-  if (fc < 0) {
-    PlanOverride ov[16];
-    const int nov = plan_overrides(ov, 16);
-    for (int i = 0; i < nov; ++i) {
-      const PlanOverride& o = ov[i];
-      if (o.qtype != qtype || o.N != N || o.K != K) continue;
-      const int S = allow_split ? o.S : 1;
-      const int64_t sps = cdiv(SB, S);
-      const int max_tb = qgemm_cfg_max_tb(o.cfg);
-      const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
-      const int64_t n_tiles = cdiv(N, qgemm_cfg_rows(o.cfg)), m_tiles = cdiv(M, 16 * tb);
-      if (cdiv(SB, sps) != S || (S > 1 && (S + 3) * M * N * 4 >= ((int64_t)1 << 32))) break;
-      return Plan{tb, o.cfg, n_tiles, m_tiles, S, (int)sps};
-    }
-    for (const Tuned& t : kTuned) {
-      if (t.qtype != qtype || t.N != N || t.K != K || M < t.m_lo || M > t.m_hi) continue;
-      const int S = allow_split ? t.S : 1;
-      const int64_t sps = cdiv(SB, S);
-      if (cdiv(SB, sps) != S) break;
-      const int max_tb = qgemm_cfg_max_tb(t.cfg);
-      const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
-      return Plan{tb, t.cfg, cdiv(N, qgemm_cfg_rows(t.cfg)), cdiv(M, 16 * tb), S, (int)sps};
-    }
+  for (const Tuned& t : kTuned) {
+    if (t.qtype != qtype || t.N != N || t.K != K || M < t.m_lo || M > t.m_hi) continue;
+    return make_plan(t.cfg, allow_split ? t.S : 1, N, K, M);
   }
   for (int cfg : {7, 6, 5, 4, 3, 2, 1}) {
-    if (fc >= 0 && cfg != fc) continue;
-    const int64_t rows = qgemm_cfg_rows(cfg);
-    const int64_t n_tiles = cdiv(N, rows);
-    const int max_tb = qgemm_cfg_max_tb(cfg);
-    const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
-    const int64_t m_tiles = cdiv(M, 16 * tb);
-    // per-step time scales roughly with the tokens per work-group
-    const double step_us = kCfgStepUs[cfg] * (qtype == 14 ? kCfgQ6Factor[cfg] : 1.0) *
-                           (0.25 + 0.75 * (double)tb / (double)max_tb);
     const int64_t smax = allow_split ? (SB < 16 ? SB : 16) : 1;
     for (int64_t S = 1; S <= smax; ++S) {
-      const int64_t sps = cdiv(SB, S);
-      const int64_t s_eff = cdiv(SB, sps);
-      if (s_eff != S) continue;
+      const Plan pl = make_plan(cfg, (int)S, N, K, M);
+      if (pl.S != S) continue;
       // the reduction reads the partials through 32-bit buffer offsets
       if (S > 1 && (S + 3) * M * N * 4 >= ((int64_t)1 << 32)) break;
-      const int64_t wgs = n_tiles * m_tiles * S;
+      const int max_tb = qgemm_cfg_max_tb(cfg);
+      // per-step time scales roughly with the tokens per work-group
+      const double step_us = kCfgStepUs[cfg] * (qtype == 14 ? kCfgQ6Factor[cfg] : 1.0) *
+                             (0.25 + 0.75 * (double)pl.tb / (double)max_tb);
+      const int64_t wgs = pl.n_tiles * pl.m_tiles * S;
       const int64_t rounds = cdiv(wgs, kCUs);
-      double cost = (double)rounds * (double)sps * step_us;
+      double cost = (double)rounds * (double)pl.sps * step_us;
       if (S > 1) cost += 2.4 + (double)S * (double)M * (double)N * 4.0 * 0.54e-6;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
-        best = Plan{tb, cfg, n_tiles, m_tiles, (int)S, (int)sps};
+        best = pl;
       }
     }
   }
   return best;
+}
+
+// Launch a planned GEMM: y directly, or split partials in the workspace and
+// their reduction.
+int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
+             const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
+             hipStream_t s) {
+  GemmParams p;
+  p.w = (const uint8_t*)w;
+  p.xq = (const uint8_t*)x_q8k;
+  p.dmax = x_dmax;
+  p.keys = nullptr;
+  p.stats = nullptr;
+  p.N = N;
+  p.SB = K / 256;
+  p.M = M;
+  p.sps = pl.sps;
+  const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
+  auto launch = [&]() { return launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s); };
+  int rc;
+  if (pl.S == 1) {
+    p.out = y;
+    p.ldo = ldy;
+    p.split_stride = 0;
+    p.bias = bias;
+    if ((rc = hip_status(launch(), fn))) return rc;
+    return ok();
+  }
+  p.out = (float*)workspace;
+  p.ldo = N;
+  p.split_stride = M * N;
+  p.bias = nullptr;  // the reduction adds it once
+  if ((rc = hip_status(launch(), fn))) return rc;
+  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, bias, s), fn);
 }
 
 }  // namespace
@@ -250,7 +236,7 @@ int dllm_quantize_q8k(const float* x, int64_t M, int64_t K, int64_t ldx, void* y
   if (!aligned(x, 4) || !aligned(y_q8k, 4) || !aligned(dmax, 4))
     return fail(DLLM_E_ALIGN, "dllm_quantize_q8k: x, y and dmax must be 4-byte aligned");
   if (M > 0x7fffffffLL) return fail(DLLM_E_SHAPE, "dllm_quantize_q8k: M=%lld exceeds 2^31-1", (long long)M);
-  return hip_status(launch_quantize_q8k(x, ldx, nullptr, M, K / 256, (uint8_t*)y_q8k, dmax, (hipStream_t)stream),
+  return hip_status(launch_quantize_q8k(x, ldx, nullptr, 0, M, K / 256, (uint8_t*)y_q8k, dmax, (hipStream_t)stream),
                     "dllm_quantize_q8k launch");
 }
 
@@ -357,32 +343,7 @@ static int qgemm_impl(const char* fn, int qtype, const void* w, int64_t N, int64
   const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
   if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     pl = plan_gemm(qtype, N, K, M, false);  // no usable workspace: whole K range per work-group
-  GemmParams p;
-  p.w = (const uint8_t*)w;
-  p.xq = (const uint8_t*)x_q8k;
-  p.dmax = x_dmax;
-  p.keys = nullptr;
-  p.stats = nullptr;
-  p.N = N;
-  p.SB = K / 256;
-  p.M = M;
-  p.sps = pl.sps;
-  hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
-  if (pl.S == 1) {
-    p.out = y;
-    p.ldo = ldy;
-    p.split_stride = 0;
-    p.bias = bias;
-    if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn))) return rc;
-    return ok();
-  }
-  p.out = (float*)workspace;
-  p.ldo = N;
-  p.split_stride = M * N;
-  p.bias = nullptr;  // the reduction adds it once
-  if ((rc = hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn))) return rc;
-  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, bias, s), fn);
+  return run_plan(fn, qtype, pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, (hipStream_t)stream);
 }
 
 int dllm_qgemm(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax, int64_t M,
@@ -414,18 +375,13 @@ int64_t dllm_lmhead_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t n_r
          lmhead_slots(N) * n_rows * 8;
 }
 
-// DLLM_LMHEAD_TILED=1 selects the tiled GEMM path even where the streaming
-// kernel applies (for testing both).
-static bool lmhead_force_tiled() {
-  const char* e = getenv("DLLM_LMHEAD_TILED");
-  return e && e[0] == '1' && !e[1];
-}
-
 // dllm_lmhead_masked, and with lse / p_max (both or neither) dllm_lmhead_confidence.
+// path: 0 chooses (the streaming kernel where it applies), 1 forces the
+// streaming kernel, 2 the tiled GEMM with the argmax epilogue.
 static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M,
                        int64_t ldh, const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl,
                        int32_t* argmax, float* lse, float* p_max, void* workspace, int64_t workspace_bytes,
-                       void* stream) {
+                       int path, void* stream) {
   int rc = check_qtype(qtype);
   if (rc) return rc;
   if (!w || !h || !rows || !logits || !argmax || !workspace)
@@ -453,14 +409,18 @@ static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int6
   if (workspace_bytes < need)
     return fail(DLLM_E_WORKSPACE, "%s: workspace of %lld bytes, need %lld", fn, (long long)workspace_bytes,
                 (long long)need);
+  if (path < 0 || path > 2) return fail(DLLM_E_ARG, "%s: path=%d must be 0, 1 or 2", fn, path);
+  if (path == 1 && !lmhead_stream_fits(K, n_rows))
+    return fail(DLLM_E_SHAPE, "%s: the streaming LM head takes K <= 4096 and n_rows <= 32 (K=%lld, n_rows=%lld)", fn,
+                (long long)K, (long long)n_rows);
   hipStream_t s = (hipStream_t)stream;
   const int64_t SB = K / 256;
   uint8_t* xq = (uint8_t*)workspace;
   uint64_t* keys = (uint64_t*)((uint8_t*)workspace + align256(n_rows * SB * Q8K_BYTES));
   float2* stats = lse ? (float2*)((uint8_t*)keys + align256(lmhead_slots(N) * n_rows * 8)) : nullptr;
-  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, n_rows, SB, xq, nullptr, s), "lm head gather/quantize launch")))
+  if ((rc = hip_status(launch_quantize_q8k(h, ldh, rows, M, n_rows, SB, xq, nullptr, s), "lm head gather/quantize launch")))
     return rc;
-  if (lmhead_stream_fits(K, n_rows) && !lmhead_force_tiled()) {
+  if (path != 2 && lmhead_stream_fits(K, n_rows)) {
     LmParams lp;
     lp.w = (const uint8_t*)w;
     lp.xq = xq;
@@ -500,7 +460,7 @@ int dllm_lmhead_masked(int qtype, const void* w, int64_t N, int64_t K, const flo
                        const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax,
                        void* workspace, int64_t workspace_bytes, void* stream) {
   return lmhead_impl("dllm_lmhead_masked", qtype, w, N, K, h, M, ldh, rows, n_rows, logits, ldl, argmax, nullptr,
-                     nullptr, workspace, workspace_bytes, stream);
+                     nullptr, workspace, workspace_bytes, 0, stream);
 }
 
 int dllm_lmhead_confidence(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
@@ -509,7 +469,7 @@ int dllm_lmhead_confidence(int qtype, const void* w, int64_t N, int64_t K, const
   if (!lse || !p_argmax)
     return fail(DLLM_E_ARG, "dllm_lmhead_confidence: null pointer (lse=%p, p_argmax=%p)", (void*)lse, (void*)p_argmax);
   return lmhead_impl("dllm_lmhead_confidence", qtype, w, N, K, h, M, ldh, rows, n_rows, logits, ldl, argmax, lse,
-                     p_argmax, workspace, workspace_bytes, stream);
+                     p_argmax, workspace, workspace_bytes, 0, stream);
 }
 
 int dllm_qgemm_partials_i32(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M, int32_t* P,
@@ -523,6 +483,72 @@ int dllm_qgemm_partials_i32(int qtype, const void* w, int64_t N, int64_t K, cons
   return hip_status(launch_partials(qtype, (const uint8_t*)w, N, K / 256, (const uint8_t*)x_q8k, M, P,
                                     (hipStream_t)stream),
                     "dllm_qgemm_partials_i32 launch");
+}
+
+// ---- test-only entry points ------------------------------------------------
+
+int dllm_qgemm_planned(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax,
+                       int64_t M, const float* bias, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                       int tile, int split, void* stream) {
+  const char* fn = "dllm_qgemm_planned";
+  int rc = check_gemm_args(fn, qtype, w, N, K, x_q8k, M);
+  if (rc) return rc;
+  if (!y) return fail(DLLM_E_ARG, "%s: null output pointer", fn);
+  if (ldy < N) return fail(DLLM_E_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (!aligned(y, 4) || !aligned(x_dmax, 4) || !aligned(bias, 4))
+    return fail(DLLM_E_ALIGN, "%s: y, x_dmax and bias must be 4-byte aligned", fn);
+  if (tile < 1 || tile > 7) return fail(DLLM_E_ARG, "%s: tile=%d must be 1..7", fn, tile);
+  if (split < 1 || split > K / 256) return fail(DLLM_E_ARG, "%s: split=%d must be in [1, K/256]", fn, split);
+  const Plan pl = make_plan(tile, split, N, K, M);
+  if (pl.S > 1) {
+    if ((pl.S + 3) * M * N * 4 >= ((int64_t)1 << 32))
+      return fail(DLLM_E_SHAPE, "%s: %d partial slices of %lld x %lld are too large", fn, pl.S, (long long)M,
+                  (long long)N);
+    const int64_t need = (int64_t)pl.S * M * N * 4;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+      return fail(DLLM_E_WORKSPACE, "%s: split %d needs a 16-byte aligned workspace of %lld bytes", fn, pl.S,
+                  (long long)need);
+  }
+  return run_plan(fn, qtype, pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, (hipStream_t)stream);
+}
+
+int dllm_lmhead_planned(int qtype, const void* w, int64_t N, int64_t K, const float* h, int64_t M, int64_t ldh,
+                        const int32_t* rows, int64_t n_rows, float* logits, int64_t ldl, int32_t* argmax, float* lse,
+                        float* p_argmax, void* workspace, int64_t workspace_bytes, int path, void* stream) {
+  return lmhead_impl("dllm_lmhead_planned", qtype, w, N, K, h, M, ldh, rows, n_rows, logits, ldl, argmax, lse,
+                     p_argmax, workspace, workspace_bytes, path, stream);
+}
+
+int dllm_qgemm_superblock_sums_i32(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, int64_t M,
+                                   int32_t* A, int tile, int split, void* stream) {
+  const char* fn = "dllm_qgemm_superblock_sums_i32";
+  int rc = check_gemm_args(fn, qtype, w, N, K, x_q8k, M);
+  if (rc) return rc;
+  if (!A) return fail(DLLM_E_ARG, "%s: null output pointer", fn);
+  if (!aligned(A, 4)) return fail(DLLM_E_ALIGN, "%s: A must be 4-byte aligned", fn);
+  if (tile < 1 || tile > 7) return fail(DLLM_E_ARG, "%s: tile=%d must be 1..7", fn, tile);
+  if (split < 1 || split > K / 256) return fail(DLLM_E_ARG, "%s: split=%d must be in [1, K/256]", fn, split);
+  if (M * N * (K / 256) > ((int64_t)1 << 31)) return fail(DLLM_E_SHAPE, "%s: output too large for a test export", fn);
+  // the test form runs the configuration's largest token tile
+  Plan pl = make_plan(tile, split, N, K, M);
+  pl.tb = qgemm_cfg_max_tb(tile);
+  pl.m_tiles = cdiv(M, (int64_t)16 * pl.tb);
+  GemmParams p;
+  p.w = (const uint8_t*)w;
+  p.xq = (const uint8_t*)x_q8k;
+  p.dmax = nullptr;
+  p.out = (float*)A;
+  p.keys = nullptr;
+  p.stats = nullptr;
+  p.bias = nullptr;
+  p.N = N;
+  p.SB = K / 256;
+  p.M = M;
+  p.ldo = N;
+  p.split_stride = 0;
+  p.sps = pl.sps;
+  const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
+  return hip_status(launch_qgemm_sums(qtype, p, tile, grid, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

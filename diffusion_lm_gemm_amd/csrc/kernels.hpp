@@ -32,8 +32,9 @@ struct LmParams {
   int64_t ldl;
 };
 
-hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
-                               float* dmax, hipStream_t s);
+// rows (or null): output row m quantizes x row rows[m], clamped into [0, n_src).
+hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t n_src, int64_t M, int64_t SB,
+                               uint8_t* y, float* dmax, hipStream_t s);
 // Fused producers (RMSNorm -> Q8_K with K <= 16384, SwiGLU -> Q8_K; see quantize.hip).
 bool rmsnorm_quantize_fits(int64_t SB);
 hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, int64_t SB, const float* g, float eps,
@@ -55,6 +56,9 @@ hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* o
 int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
+// The same kernels in their test form: the exact int32 super-block sums
+// A[m][n][sb] go to p.out instead of y; token tile qgemm_cfg_max_tb(cfg).
+hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s);
 // y = the sum of the S partial slices, plus bias[n] per column when bias is not null.
 hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
                                hipStream_t s);

@@ -46,7 +46,10 @@ namespace dllm {
 // ST = 1: one stage, loaded at the start of each step (two barriers per
 // step); with 4 waves this fits two work-groups per CU whose waits the other
 // one's work fills.
-template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
+// SUMS: the test form of the same kernel, which also stores every tile's
+// exact int32 super-block sums A_sb = (hi << shift) + lo, as formed for the
+// epilogue, to ((int32_t*)p.out)[(m * N + n) * SB + sb], and writes no y.
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
   static_assert(NW == 4 || NW == 8 || NW == 12, "waves per work-group: 4, 8 or 12 (whole SIMDs)");
   constexpr bool ONE = (ST == 1);
@@ -114,6 +117,21 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     row_ok[b] = nrow < N;
     wrow_off[b] = (uint32_t)(nrow * SB * BYTES);
   }
+
+  // SUMS: a lane's integer tile sums are rows row0 + 16 b + 4 g4 + i of
+  // token m0 + 16 t + r
+  auto sums_store = [&](int t, int b, int64_t sb, const v4i& al, const v4i& ah) {
+    if constexpr (SUMS) {
+      const int64_t m = m0 + t * 16 + r;
+      const int64_t nb = row0 + 16 * b + 4 * g4;
+      int32_t* P = (int32_t*)p.out;
+      if (m < M) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nb + i < N) P[(m * N + nb + i) * SB + sb] = (ah[i] << SHIFT) + al[i];
+      }
+    }
+  };
 
   // ---- activation staging.  The int8 quants go global -> LDS directly:
   // load k of wave wv fills LDS units (wv DPW + k) 64 + lane, i.e. token
@@ -260,6 +278,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + bunit[c]);
     };
     auto flush = [&](int t, int b, const v4i& al, const v4i& ah) {
+      sums_store(t, b, sb, al, ah);
       const float dx = s_dx[buf][t * 16 + r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -382,6 +401,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
     for (int t = 0; t < TB; ++t) dxr[t] = s_dx[buf][t * 16 + r];
     auto flush = [&](int t, const v4i& al, const v4i& ah) {
+      sums_store(t, 0, sb, al, ah);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = (ah[i] << SHIFT) + al[i];
@@ -547,6 +567,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // ---- write out: lane holds rows nbase + i (i < 4) of token t*16 + r
   // (plus the bias of those rows, when given: only without a K split, whose
   // reduction adds it instead)
+  if constexpr (SUMS) return;
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
@@ -767,9 +788,9 @@ __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w,
 }
 
 // ---- host-side launch helpers -------------------------------------------
-template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2>
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
 static hipError_t launch_k(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX, ST>), grid, dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX, ST, SUMS>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -825,6 +846,25 @@ static hipError_t launch_cfg(const GemmParams& p, int tb, int cfg, dim3 grid, bo
     case 4: return c3 ? launch_k<QT, 4, 8, 2, false>(p, grid, s) : launch_k<QT, 4, 4, 2, false>(p, grid, s);
     default: return c3 ? launch_k<QT, 5, 8, 2, false>(p, grid, s) : launch_k<QT, 5, 4, 2, false>(p, grid, s);
   }
+}
+
+// The SUMS form of each tile configuration, at its largest token tile.
+template <int QT>
+static hipError_t launch_sums_cfg(const GemmParams& p, int cfg, dim3 grid, hipStream_t s) {
+  switch (cfg) {
+    case 1: return launch_k<QT, 10, 4, 1, false, 2, true>(p, grid, s);
+    case 2: return launch_k<QT, 10, 8, 1, false, 2, true>(p, grid, s);
+    case 3: return launch_k<QT, 5, 8, 2, false, 2, true>(p, grid, s);
+    case 4: return launch_k<QT, 5, 4, 2, false, 2, true>(p, grid, s);
+    case 5: return launch_k<QT, 10, 4, 1, false, 1, true>(p, grid, s);
+    case 6: return launch_k<QT, 5, 4, 1, false, 2, true>(p, grid, s);
+    default: return launch_k<QT, 5, 12, 1, false, 2, true>(p, grid, s);
+  }
+}
+
+hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s) {
+  if (qtype == QT_Q4K) return launch_sums_cfg<QT_Q4K>(p, cfg, grid, s);
+  return launch_sums_cfg<QT_Q6K>(p, cfg, grid, s);
 }
 
 int qgemm_cfg_rows(int cfg) {

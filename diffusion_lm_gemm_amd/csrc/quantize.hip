@@ -119,6 +119,7 @@ struct QuantArgs {
   const float* x;
   int64_t ldx;
   const int32_t* rows;  // PLAIN: gather rows[m] (or null)
+  int64_t n_src;        // with rows: rows of x; an index outside [0, n_src) is clamped into it
   int64_t SB;           // blocks per output row
   uint8_t* y;
   float* dmax;          // per row, the largest |d| (or null)
@@ -147,7 +148,11 @@ __global__ __launch_bounds__(64 * QW) void k_quantize_q8k(QuantArgs a) {
   __shared__ float s_r;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t m = blockIdx.x, SB = a.SB, K = SB * QK;
-  const int64_t src_row = (MODE == Q_PLAIN && a.rows) ? (int64_t)a.rows[m] : m;
+  int64_t src_row = m;
+  if (MODE == Q_PLAIN && a.rows) {
+    const int64_t i = (int64_t)a.rows[m];
+    src_row = i < 0 ? 0 : (i >= a.n_src ? a.n_src - 1 : i);  // never a read outside x
+  }
   const float* xrow = a.x + src_row * a.ldx;
   // every lane's 16 bytes are aligned exactly when the row start is
   const bool vec = ((((uintptr_t)xrow) & 15) == 0) && (MODE != Q_SWIGLU || (K & 3) == 0);
@@ -243,21 +248,21 @@ static hipError_t launch_mode(const QuantArgs& a, int64_t M, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t M, int64_t SB, uint8_t* y,
-                               float* dmax, hipStream_t s) {
-  return launch_mode<Q_PLAIN>(QuantArgs{x, ldx, rows, SB, y, dmax, nullptr, 0.0f}, M, s);
+hipError_t launch_quantize_q8k(const float* x, int64_t ldx, const int32_t* rows, int64_t n_src, int64_t M, int64_t SB,
+                               uint8_t* y, float* dmax, hipStream_t s) {
+  return launch_mode<Q_PLAIN>(QuantArgs{x, ldx, rows, n_src, SB, y, dmax, nullptr, 0.0f}, M, s);
 }
 
 bool rmsnorm_quantize_fits(int64_t SB) { return SB <= RMS_SBMAX; }
 
 hipError_t launch_rmsnorm_quantize_q8k(const float* x, int64_t ldx, int64_t M, int64_t SB, const float* g, float eps,
                                        uint8_t* y, float* dmax, hipStream_t s) {
-  return launch_mode<Q_RMSNORM>(QuantArgs{x, ldx, nullptr, SB, y, dmax, g, eps}, M, s);
+  return launch_mode<Q_RMSNORM>(QuantArgs{x, ldx, nullptr, 0, SB, y, dmax, g, eps}, M, s);
 }
 
 hipError_t launch_swiglu_quantize_q8k(const float* gu, int64_t ldgu, int64_t M, int64_t SB, uint8_t* y, float* dmax,
                                       hipStream_t s) {
-  return launch_mode<Q_SWIGLU>(QuantArgs{gu, ldgu, nullptr, SB, y, dmax, nullptr, 0.0f}, M, s);
+  return launch_mode<Q_SWIGLU>(QuantArgs{gu, ldgu, nullptr, 0, SB, y, dmax, nullptr, 0.0f}, M, s);
 }
 
 }  // namespace dllm

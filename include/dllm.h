@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 6
+#define DLLM_ABI_VERSION 8
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -186,8 +186,10 @@ int dllm_qgemm_bias(int qtype, const void *w, int64_t N, int64_t K,
  * w [N][K] and write f32 logits plus the per-row argmax (greedy pick; lowest
  * index among exactly equal logits).
  *   h       f32 [M][ldh], ldh >= K
- *   rows    int32 [n_rows] device array, each in [0, M) (not checked on the
- *           host: an out-of-range index is undefined behaviour)
+ *   rows    int32 [n_rows] device array, each in [0, M); the device code
+ *           clamps an index outside [0, M) to the nearest valid row (the
+ *           result for that row is then meaningless, but nothing outside h
+ *           is read)
  *   logits  f32 [n_rows][ldl], ldl >= N (written)
  *   argmax  int32 [n_rows] (written)
  *   workspace  at least dllm_lmhead_workspace_bytes(qtype, N, K, n_rows) bytes,
@@ -229,12 +231,60 @@ int dllm_lmhead_confidence(int qtype, const void *w, int64_t N, int64_t K,
  * Test export: per-16 integer partial dots of the shared form,
  * P[m][n][sb][g] = sum_{t<16} u[n][256 sb + 16 g + t] * q[m][256 sb + 16 g + t]
  * (u: the unsigned shared-form quant, q: the Q8_K int8 quant), int32, written
- * as [M][N][K/256][16].  Uses the same in-register unpacking as dllm_qgemm.
- * Meant for small shapes.
+ * as [M][N][K/256][16].  Computed by a separate reference kernel (v_dot4 on
+ * the quants taken from the GGUF bit layout), not by the matrix kernels; the
+ * matrix kernels' own integer sums are checked through
+ * dllm_qgemm_superblock_sums_i32.  Meant for small shapes.
  */
 int dllm_qgemm_partials_i32(int qtype, const void *w, int64_t N, int64_t K,
                             const void *x_q8k, int64_t M, int32_t *P,
                             void *stream);
+
+/*
+ * Test export: the exact int32 super-block sums the matrix kernel forms from
+ * its two int8 planes (Development plan, "Compute design": the per-16 integer
+ * scale form), A[m][n][sb] = (hi << shift) + lo, written as [M][N][K/256]:
+ *   Q4_K: A = sum_{j<8} sc_j * sum_{t<32} u[32j + t] q[32j + t]
+ *   Q6_K: A = sum_{g<16} sc_g * sum_{t<16} (u[16g + t] - 32) q[16g + t]
+ * (sc the sub-block scales, u the shared-form quants, q the Q8_K quants of
+ * super-block sb).  It launches dllm_qgemm's own kernel for tile
+ * configuration `tile` (1..7) and K split `split` (1..K/256), in a compiled
+ * form that stores each tile's integer sums where it would fold them into y;
+ * the unpacking, the v_mfma_i32_16x16x64_i8 contraction and the loop are the
+ * same code.  The token tile is the configuration's largest.  Meant for small
+ * shapes (M * N * K/256 <= 2^31); DLLM_E_ARG for a bad tile or split.
+ */
+int dllm_qgemm_superblock_sums_i32(int qtype, const void *w, int64_t N,
+                                   int64_t K, const void *x_q8k, int64_t M,
+                                   int32_t *A, int tile, int split,
+                                   void *stream);
+
+/*
+ * Test-only entry points with the kernel choice made explicit (for checking
+ * every tile configuration and both LM-head paths; the product calls above
+ * choose by themselves and read no environment).
+ *
+ * dllm_qgemm_planned: dllm_qgemm_bias with a given tile configuration and K
+ *   split: tile 1..7 (the work-group shapes of the 16 x 16 tiles); split in
+ *   [1, K/256] (reduced to the number of non-empty splits).  A split S > 1
+ *   needs a 16-byte aligned workspace of S * M * N * 4 bytes (DLLM_E_WORKSPACE
+ *   otherwise).  The result agrees with dllm_qgemm to f32 rounding.
+ * dllm_lmhead_planned: dllm_lmhead_confidence (lse and p_argmax may both be
+ *   NULL: dllm_lmhead_masked) with path 0 (choose), 1 (the streaming kernel;
+ *   K <= 4096 and n_rows <= 32, DLLM_E_SHAPE otherwise) or 2 (the tiled GEMM
+ *   with the argmax epilogue).
+ */
+int dllm_qgemm_planned(int qtype, const void *w, int64_t N, int64_t K,
+                       const void *x_q8k, const float *x_dmax, int64_t M,
+                       const float *bias, float *y, int64_t ldy,
+                       void *workspace, int64_t workspace_bytes, int tile,
+                       int split, void *stream);
+int dllm_lmhead_planned(int qtype, const void *w, int64_t N, int64_t K,
+                        const float *h, int64_t M, int64_t ldh,
+                        const int32_t *rows, int64_t n_rows, float *logits,
+                        int64_t ldl, int32_t *argmax, float *lse,
+                        float *p_argmax, void *workspace,
+                        int64_t workspace_bytes, int path, void *stream);
 
 #ifdef __cplusplus
 }

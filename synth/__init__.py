@@ -17,6 +17,10 @@ Stand-in for the model weights and prompts of the mojo-dllm pages
   f16 d at the end drawn U(1e-3, 1e-2).
 * Activations / hidden states: f32 N(0, 1).
 
+Edge-case variants (for parity over the whole range the formats allow):
+Q6_K scales over all of -128..127, and Q4_K d / dmin log-uniform over many
+decades, down into the f16 subnormals.
+
 Every tensor is keyed by (seed, name): the name is hashed into the generator
 seed, so any tensor can be regenerated on its own.  On a CUDA/HIP device the
 bytes come from torch's device generator (fast, for multi-GB weight sets); on
@@ -27,6 +31,7 @@ from __future__ import annotations
 
 import hashlib
 
+import numpy as np
 import torch
 
 QK_K = 256
@@ -57,22 +62,29 @@ def _f16_bytes(vals_f32: torch.Tensor) -> torch.Tensor:
     return vals_f32.to(torch.float16).contiguous().view(torch.uint8).view(-1, 2)
 
 
-def _uniform_f16(n: int, lo: float, hi: float, g, device) -> torch.Tensor:
-    u = torch.rand(n, generator=g, device=device, dtype=torch.float32)
-    return _f16_bytes(lo + (hi - lo) * u)
+def _uniform_f16(n: int, lo: float, hi: float, g, device, log: bool = False) -> torch.Tensor:
+    """n values U(lo, hi) -- or, with `log`, log-uniform on [lo, hi] -- as f16
+    bit patterns (values below 2^-14 become f16 subnormals)."""
+    u = torch.rand(n, generator=g, device=device, dtype=torch.float64)
+    if log:
+        v = torch.exp(np.log(lo) + (np.log(hi) - np.log(lo)) * u)
+    else:
+        v = lo + (hi - lo) * u
+    return _f16_bytes(v.to(torch.float32))
 
 
 def q4k_rows(n_rows: int, K: int, seed: int, name: str, device="cpu",
-             d_range=(1e-3, 1e-2), dmin_range=(1e-3, 1e-2)) -> torch.Tensor:
-    """uint8 tensor [n_rows, K/256*144]: seeded random Q4_K super-blocks."""
+             d_range=(1e-3, 1e-2), dmin_range=(1e-3, 1e-2), log: bool = False) -> torch.Tensor:
+    """uint8 tensor [n_rows, K/256*144]: seeded random Q4_K super-blocks;
+    `log` draws d and dmin log-uniform over their ranges instead."""
     assert K % QK_K == 0
     sb = K // QK_K
     g = _gen(seed, name, device)
     blk = torch.randint(0, 256, (n_rows * sb, Q4_K_BYTES), generator=g,
                         device=device, dtype=torch.uint8)
     nb = n_rows * sb
-    blk[:, 0:2] = _uniform_f16(nb, *d_range, g, device)
-    blk[:, 2:4] = _uniform_f16(nb, *dmin_range, g, device)
+    blk[:, 0:2] = _uniform_f16(nb, *d_range, g, device, log)
+    blk[:, 2:4] = _uniform_f16(nb, *dmin_range, g, device, log)
     return blk.view(n_rows, sb * Q4_K_BYTES)
 
 
@@ -91,6 +103,23 @@ def q6k_rows(n_rows: int, K: int, seed: int, name: str, device="cpu",
     blk[:, 192:208] = sc.to(torch.int8).view(torch.uint8)
     blk[:, 208:210] = _uniform_f16(nb, *d_range, g, device)
     return blk.view(n_rows, sb * Q6_K_BYTES)
+
+
+def q6k_rows_full_range(n_rows: int, K: int, seed: int, name: str) -> torch.Tensor:
+    """Q6_K rows (CPU) with scales uniform on all of -128..127; in every row
+    the first block has the extremes -128 and 127 planted (alternating), the
+    second (when there is one) only scales in 64..127 and the third only
+    -128..-65."""
+    w = q6k_rows(n_rows, K, seed, name, scale_range=(-128, 127))
+    blk = w.view(n_rows, K // QK_K, Q6_K_BYTES)
+    sc = blk[:, :, 192:208].view(torch.int8)
+    sc[:, 0, :] = torch.tensor([-128, 127] * 8, dtype=torch.int8)
+    g = _gen(seed, name + "/planted", "cpu")
+    if K // QK_K > 1:
+        sc[:, 1, :] = torch.randint(64, 128, (n_rows, 16), generator=g).to(torch.int8)
+    if K // QK_K > 2:
+        sc[:, 2, :] = torch.randint(-128, -64, (n_rows, 16), generator=g).to(torch.int8)
+    return w
 
 
 def qk_rows(qtype: int, n_rows: int, K: int, seed: int, name: str, device="cpu"):

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -187,3 +187,48 @@ def test_workspace_queries(dl):
     assert dl.qgemm_workspace_bytes(dl.Q6_K, 126464, 4096, 32) == 0
     assert dl.qgemm_workspace_bytes(99, 4096, 4096, 148) == -1
     assert dl.lmhead_workspace_bytes(dl.Q6_K, 126464, 4096, 32) >= 32 * 16 * 292
+
+
+def test_test_entry_argument_errors(dl):
+    """The test-only entry points validate their explicit kernel choice on
+    the host: tile configuration 1..7, K split 1..K/256, LM-head path 0..2
+    (the streaming path only where it applies), a workspace for a split."""
+    L = dl.lib
+    big = 1 << 30
+    for tile in (0, 8, 32):
+        assert L.dllm_qgemm_planned(dl.Q4_K, FAKE, 64, 1024, FAKE, None, 4, None, FAKE, 64, FAKE, big, tile, 1,
+                                    None) == dl.E_ARG
+        assert "tile" in dl.last_error()
+        assert L.dllm_qgemm_superblock_sums_i32(dl.Q6_K, FAKE, 64, 1024, FAKE, 4, FAKE, tile, 1, None) == dl.E_ARG
+    for split in (0, 5):
+        assert L.dllm_qgemm_planned(dl.Q4_K, FAKE, 64, 1024, FAKE, None, 4, None, FAKE, 64, FAKE, big, 1, split,
+                                    None) == dl.E_ARG
+        assert "split" in dl.last_error()
+        assert L.dllm_qgemm_superblock_sums_i32(dl.Q4_K, FAKE, 64, 1024, FAKE, 4, FAKE, 1, split, None) == dl.E_ARG
+    # a split needs a 16-byte aligned workspace of S * M * N * 4 bytes
+    assert L.dllm_qgemm_planned(dl.Q4_K, FAKE, 64, 1024, FAKE, None, 4, None, FAKE, 64, None, 0, 1, 2,
+                                None) == dl.E_WORKSPACE
+    assert L.dllm_qgemm_planned(dl.Q4_K, FAKE, 64, 1024, FAKE, None, 4, None, FAKE, 64, FAKE, 2 * 4 * 64 * 4 - 1, 1,
+                                2, None) == dl.E_WORKSPACE
+    ok_ws = dl.lmhead_workspace_bytes(dl.Q6_K, 1000, 512, 4)
+    ws = ctypes.c_void_p(1 << 24)
+    for path in (-1, 3):
+        assert L.dllm_lmhead_planned(dl.Q6_K, FAKE, 1000, 512, FAKE, 8, 512, FAKE, 4, FAKE, 1000, FAKE, None, None,
+                                     ws, ok_ws, path, None) == dl.E_ARG
+        assert "path" in dl.last_error()
+    # the streaming kernel takes K <= 4096 and at most 32 rows
+    ok_ws = dl.lmhead_workspace_bytes(dl.Q6_K, 1000, 8192, 4)
+    assert L.dllm_lmhead_planned(dl.Q6_K, FAKE, 1000, 8192, FAKE, 8, 8192, FAKE, 4, FAKE, 1000, FAKE, None, None,
+                                 ws, ok_ws, 1, None) == dl.E_SHAPE
+    ok_ws = dl.lmhead_workspace_bytes(dl.Q6_K, 1000, 512, 40)
+    assert L.dllm_lmhead_planned(dl.Q6_K, FAKE, 1000, 512, FAKE, 48, 512, FAKE, 40, FAKE, 1000, FAKE, None, None,
+                                 ws, ok_ws, 1, None) == dl.E_SHAPE
+
+
+def test_no_environment_reads_in_the_library():
+    """Kernel choice is made by arguments and compiled tables only: the
+    library sources read no environment variables."""
+    csrc = os.path.join(ROOT, "diffusion_lm_gemm_amd", "csrc")
+    for name in os.listdir(csrc):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            assert "getenv" not in open(os.path.join(csrc, name)).read(), name

@@ -151,7 +151,7 @@ def test_dream_lmhead_every_masked_row(dl):
                       "dream lmhead confidence")
 
 
-def test_dream_lmhead_block_of_32_streams(dl, monkeypatch):
+def test_dream_lmhead_block_of_32_streams(dl):
     """A block of 32 masked rows at Dream's head takes the streaming kernel
     (K = 3584 is 14 super-blocks, 152 064 rows): whole logits, argmax and
     confidence against the oracle, and the tiled path on the same rows."""
@@ -167,8 +167,7 @@ def test_dream_lmhead_block_of_32_streams(dl, monkeypatch):
     _check_argmax(lg, am, ref, ref_am, "dream lmhead 32 rows")
     _check_confidence(lg, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
                       "dream lmhead 32 rows confidence")
-    monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
-    lg_t, am_t = dl.lmhead_masked(14, wd, N, K, hd, rd)
+    lg_t, am_t, _, _ = dl.lmhead_planned(14, wd, N, K, hd, rd, path=2, confidence=False)
     lg_t = lg_t.cpu().numpy(); am_t = am_t.cpu().numpy()
     assert_close_rows(lg_t, ref, "dream lmhead 32 rows, tiled path")
     _check_argmax(lg_t, am_t, ref, ref_am, "dream lmhead 32 rows, tiled path")

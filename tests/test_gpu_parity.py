@@ -277,27 +277,28 @@ def test_qgemm_small_shapes(dl, qtype, M, N, K, split):
     assert_close_rows(y, ref, f"qgemm {qtype} {M}x{N}x{K} split={split}")
 
 
+TILES = (1, 2, 3, 4, 5, 6, 7)
+
+
 @pytest.mark.parametrize("qtype", [12, 14])
-@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6", "7"])
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", [(148, 333, 2048), (37, 130, 1024), (160, 256, 512)])
-def test_qgemm_every_tile_configuration(dl, monkeypatch, qtype, tile, M, N, K):
+def test_qgemm_every_tile_configuration(dl, qtype, tile, M, N, K):
     """Each work-group shape (64 rows as 4 waves x 16, 128 rows as 8 waves x
     16, and over at most 80 tokens 256 rows as 8 waves x 32 or 128 rows as 4
     waves x 32; 64 rows as 4 waves x 16 with one activation stage; 64 rows as
     4 waves x 16 over at most 80 tokens; 192 rows as 12 waves x 16 over at
-    most 80 tokens), pinned through DLLM_QGEMM_TILE, on ragged rows and
-    tokens, split and unsplit."""
-    monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
+    most 80 tokens), chosen through the test entry dllm_qgemm_planned, on
+    ragged rows and tokens, split and unsplit."""
     _say(f"qgemm tile={tile} qtype={qtype} M={M} N={N} K={K}")
     w = _weights(qtype, N, K, 11, f"t-{N}-{K}")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 11, f"tx-{M}-{K}").numpy())
     ref = oracle.gemm(qtype, w.numpy(), N, K, xq, M)
-    ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
     xd = torch.from_numpy(xq).to(DEV)
     wd = w.to(DEV)
-    for workspace in (ws, None):
-        y = dl.qgemm(qtype, wd, N, K, xd, M, workspace=workspace).cpu().numpy()
-        assert_close_rows(y, ref, f"qgemm tile {tile} {qtype} {M}x{N}x{K} ws={workspace is not None}")
+    for split in (3, 1):
+        y = dl.qgemm_planned(qtype, wd, N, K, xd, M, tile=tile, split=split).cpu().numpy()
+        assert_close_rows(y, ref, f"qgemm tile {tile} {qtype} {M}x{N}x{K} split={split}")
 
 
 @pytest.mark.parametrize("qtype,N,K", [(12, 4096, 4096), (14, 4096, 12288)])
@@ -427,14 +428,13 @@ def test_qgemm_step_shapes(dl, qtype, N, K, M):
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("tile", ["1", "2", "3", "4", "5", "6", "7"])
-def test_qgemm_dmax_hint_matches_scan(dl, monkeypatch, tile):
+@pytest.mark.parametrize("tile", TILES)
+def test_qgemm_dmax_hint_matches_scan(dl, tile):
     """Q4_K with the per-token largest |d| from dllm_quantize_q8k: the same
     bits as without it (where the kernel reads every d itself), for every
     tile configuration, split and unsplit, on ragged shapes, with magnitudes
     spread over nine decades so the power-of-two range scale differs per
     token."""
-    monkeypatch.setenv("DLLM_QGEMM_TILE", tile)
     N, K, M = 333, 3072, 150
     _say(f"dmax hint tile={tile}")
     w = _weights(12, N, K, 23, "hint").to(DEV)
@@ -442,48 +442,43 @@ def test_qgemm_dmax_hint_matches_scan(dl, monkeypatch, tile):
     dmax = torch.empty(M, device=DEV)
     xq = dl.quantize_q8k(x.to(DEV), dmax=dmax)
     ref = oracle.gemm(12, w.cpu().numpy(), N, K, xq.cpu().numpy(), M)
-    ws = dl.qgemm_workspace(12, N, K, M, DEV)
-    for workspace in (ws, None):
-        a = dl.qgemm(12, w, N, K, xq, M, workspace=workspace, x_dmax=dmax)
-        b = dl.qgemm(12, w, N, K, xq, M, workspace=workspace)
+    for split in (4, 1):
+        a = dl.qgemm_planned(12, w, N, K, xq, M, tile=tile, split=split, x_dmax=dmax)
+        b = dl.qgemm_planned(12, w, N, K, xq, M, tile=tile, split=split)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
-        assert_close_rows(a.cpu().numpy(), ref, f"dmax hint tile {tile} ws={workspace is not None}")
+        assert_close_rows(a.cpu().numpy(), ref, f"dmax hint tile {tile} split={split}")
 
 
-@pytest.mark.parametrize("plan", ["12:333:3072:7:4", "12:333:3072:6:3", "12:333:3072:2:12"])
-def test_qgemm_plan_override(dl, monkeypatch, plan):
-    """DLLM_QGEMM_PLAN pins (tile configuration, K split) for a shape; the
-    result stays within the bound for each pinned plan."""
-    monkeypatch.setenv("DLLM_QGEMM_PLAN", plan)
+@pytest.mark.parametrize("tile,split", [(7, 4), (6, 3), (2, 12), (4, 7), (5, 5)])
+def test_qgemm_planned_splits(dl, tile, split):
+    """(tile configuration, K split) pinned through dllm_qgemm_planned: the
+    result stays within the bound for each plan, including splits whose last
+    slice is shorter (12 super-blocks over 7 and 5 slices)."""
     N, K, M = 333, 3072, 150
-    _say(f"plan override {plan}")
+    _say(f"planned tile={tile} split={split}")
     w = _weights(12, N, K, 29, "plan")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 29, "plan-x").numpy())
     ref = oracle.gemm(12, w.numpy(), N, K, xq, M)
-    ws = dl.qgemm_workspace(12, N, K, M, DEV)
-    y = dl.qgemm(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, workspace=ws).cpu().numpy()
-    assert_close_rows(y, ref, f"plan {plan}")
+    y = dl.qgemm_planned(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, tile=tile, split=split).cpu().numpy()
+    assert_close_rows(y, ref, f"planned tile={tile} split={split}")
 
 
 @pytest.mark.parametrize("N,pad,K,S", [(332, 0, 3072, 2), (332, 4, 3072, 3), (332, 0, 2560, 5), (332, 8, 3072, 6),
                                        (332, 0, 4096, 8), (332, 0, 3072, 12), (333, 0, 3072, 4), (332, 1, 3072, 2),
                                        (333, 3, 4096, 8), (333, 0, 2560, 5)])
-def test_qgemm_split_reduce_paths(dl, monkeypatch, N, pad, K, S):
+def test_qgemm_split_reduce_paths(dl, N, pad, K, S):
     """The K-split sum for fixed slice counts (2, 3, 4, 6, 8) and others (run
     time), with 16-byte stores (N and the row stride multiples of four) and
     element stores (either not), into a strided output whose padding columns
     stay untouched."""
     M = 150
-    monkeypatch.setenv("DLLM_QGEMM_PLAN", f"12:{N}:{K}:6:{S}")
-    assert dl.qgemm_workspace_bytes(12, N, K, M) == S * M * N * 4  # the pinned split is taken
     _say(f"split reduce N={N} pad={pad} S={S}")
     w = _weights(12, N, K, 31, f"red-{N}")
     xq = oracle.quantize_q8k(synth.normal_f32((M, K), 31, "red-x").numpy())
     ref = oracle.gemm(12, w.numpy(), N, K, xq, M)
-    ws = dl.qgemm_workspace(12, N, K, M, DEV)
     big = torch.full((M, N + pad), 7.0, device=DEV)
-    dl.qgemm(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, y=big[:, :N], workspace=ws)
+    dl.qgemm_planned(12, w.to(DEV), N, K, torch.from_numpy(xq).to(DEV), M, tile=6, split=S, y=big[:, :N])
     torch.cuda.synchronize()
     assert torch.all(big[:, N:] == 7.0)
     assert_close_rows(big[:, :N].cpu().numpy(), ref, f"split reduce N={N} pad={pad} S={S}")
@@ -531,21 +526,20 @@ def _check_argmax(logits_gpu, am_gpu, ref_logits, ref_am, what):
 @pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 7, 32, 40])
 @pytest.mark.parametrize("K", [768, 1024, 2560])
-def test_lmhead_small(dl, monkeypatch, qtype, tiled, n_rows, K):
+def test_lmhead_small(dl, qtype, tiled, n_rows, K):
     """Both LM-head paths: the streaming kernel (<= 32 rows, K <= 4096) and
-    the tiled GEMM (forced with DLLM_LMHEAD_TILED=1, and taken for 40 rows),
+    the tiled GEMM (forced through dllm_lmhead_planned, and taken for 40 rows),
     on a vocabulary that is not a multiple of any tile (1000 rows) and K of
     3, 4 and 10 super-blocks (the stream's three-deep load rotation then
     meets a row-block boundary at every phase)."""
-    if tiled:
-        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
     N, M = 1000, 148
     _say(f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows} K={K}")
     w = _weights(qtype, N, K, 13, f"lm-small-{qtype}")
     h = synth.normal_f32((M, K), 13, "lm-h")
     rows = synth.distinct_rows(n_rows, M, 13, f"rows-{n_rows}")
     ref, ref_am = oracle.lmhead(qtype, w.numpy(), N, K, h.numpy(), rows.numpy())
-    logits, am = dl.lmhead_masked(qtype, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    logits, am, _, _ = dl.lmhead_planned(qtype, w.to(DEV), N, K, h.to(DEV), rows.to(DEV), path=2 if tiled else 0,
+                                         confidence=False)
     logits = logits.cpu().numpy(); am = am.cpu().numpy()
     assert_close_rows(logits, ref, f"lmhead qtype={qtype} tiled={tiled} n_rows={n_rows} K={K}")
     _check_argmax(logits, am, ref, ref_am, f"lmhead n_rows={n_rows}")
@@ -603,13 +597,11 @@ def _check_confidence(logits, lse, p, ref_logits, what):
 @pytest.mark.parametrize("qtype", [12, 14])
 @pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("scale", [1.0, 0.002])
-def test_lmhead_confidence(dl, monkeypatch, qtype, tiled, scale):
+def test_lmhead_confidence(dl, qtype, tiled, scale):
     """dllm_lmhead_confidence on both LM-head paths: the same logits and
     argmax as dllm_lmhead_masked, plus the log-sum-exp and the softmax
     probability of the argmax, for peaked (scale 1) and flat (scale 0.002)
     logit rows over a ragged 1000-row vocabulary."""
-    if tiled:
-        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
     N, K, M = 1000, 2048, 148
     _say(f"lmhead confidence qtype={qtype} tiled={tiled} scale={scale}")
     w = _weights(qtype, N, K, 21, f"conf-{qtype}")
@@ -617,8 +609,9 @@ def test_lmhead_confidence(dl, monkeypatch, qtype, tiled, scale):
     rows = synth.distinct_rows(13, M, 21, "conf-rows")
     ref, ref_am = oracle.lmhead(qtype, w.numpy(), N, K, h.numpy(), rows.numpy())
     wd, hd, rd = w.to(DEV), h.to(DEV), rows.to(DEV)
-    logits, am, lse, p = dl.lmhead_confidence(qtype, wd, N, K, hd, rd)
-    logits2, am2 = dl.lmhead_masked(qtype, wd, N, K, hd, rd)
+    path = 2 if tiled else 1
+    logits, am, lse, p = dl.lmhead_planned(qtype, wd, N, K, hd, rd, path=path)
+    logits2, am2, _, _ = dl.lmhead_planned(qtype, wd, N, K, hd, rd, path=path, confidence=False)
     torch.cuda.synchronize()
     assert torch.equal(logits, logits2) and torch.equal(am, am2)
     lg = logits.cpu().numpy()

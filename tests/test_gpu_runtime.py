@@ -117,19 +117,18 @@ def test_two_streams_at_once_match_sequential(dl):
 
 
 @pytest.mark.parametrize("tiled", [False, True])
-def test_lmhead_strided_logits(dl, monkeypatch, tiled):
+def test_lmhead_strided_logits(dl, tiled):
     """Logits written through a row-strided view (ldl > N) equal the
     contiguous call's, and the padding between rows is left alone, on the
     streaming and the tiled path."""
-    if tiled:
-        monkeypatch.setenv("DLLM_LMHEAD_TILED", "1")
+    path = 2 if tiled else 1
     N, K, L = 3000, 1024, 60
     w = _weights(14, N, K, 94, "rt-lm").to(DEV)
     h = synth.normal_f32((L, K), 94, "rt-lm-h").to(DEV)
     rows = torch.tensor([3, 59, 0, 17, 42], dtype=torch.int32, device=DEV)
-    ref_lg, ref_am = dl.lmhead_masked(14, w, N, K, h, rows)
+    ref_lg, ref_am, _, _ = dl.lmhead_planned(14, w, N, K, h, rows, path=path, confidence=False)
     big = torch.full((rows.numel(), N + 12), -7.0, device=DEV)
-    lg, am = dl.lmhead_masked(14, w, N, K, h, rows, logits=big[:, :N])
+    lg, am, _, _ = dl.lmhead_planned(14, w, N, K, h, rows, path=path, confidence=False, logits=big[:, :N])
     torch.cuda.synchronize()
     assert torch.equal(big[:, :N], ref_lg) and torch.equal(am, ref_am)
     assert torch.all(big[:, N:] == -7.0)
