@@ -65,12 +65,11 @@ def _f16_bytes(vals_f32: torch.Tensor) -> torch.Tensor:
 def _uniform_f16(n: int, lo: float, hi: float, g, device, log: bool = False) -> torch.Tensor:
     """n values U(lo, hi) -- or, with `log`, log-uniform on [lo, hi] -- as f16
     bit patterns (values below 2^-14 become f16 subnormals)."""
-    u = torch.rand(n, generator=g, device=device, dtype=torch.float64)
     if log:
-        v = torch.exp(np.log(lo) + (np.log(hi) - np.log(lo)) * u)
-    else:
-        v = lo + (hi - lo) * u
-    return _f16_bytes(v.to(torch.float32))
+        u = torch.rand(n, generator=g, device=device, dtype=torch.float64)
+        return _f16_bytes(torch.exp(np.log(lo) + (np.log(hi) - np.log(lo)) * u).to(torch.float32))
+    u = torch.rand(n, generator=g, device=device, dtype=torch.float32)
+    return _f16_bytes(lo + (hi - lo) * u)
 
 
 def q4k_rows(n_rows: int, K: int, seed: int, name: str, device="cpu",
