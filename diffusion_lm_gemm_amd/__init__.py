@@ -312,7 +312,8 @@ def qgemm_planned(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tens
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     assert y.dtype == torch.float32 and y.stride(1) == 1
-    ws = torch.empty(max(split * M * N * 4, 256), dtype=torch.uint8, device=dev)
+    # the tile counters (64 KiB), then the partial slices; zero-filled
+    ws = torch.zeros(65536 + split * M * ((N + 63) // 64 * 64) * 4, dtype=torch.uint8, device=dev)
     _check(lib.dllm_qgemm_planned(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(bias), _ptr(y),
                                   y.stride(0), _ptr(ws), ws.numel(), tile, split, _stream(dev)))
     return y

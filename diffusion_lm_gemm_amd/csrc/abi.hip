@@ -74,6 +74,7 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // The GEMM kernels address weights and activations with 32-bit buffer
 // offsets: each operand (plus one tile of padding rows) must stay below 2 GiB.
@@ -105,14 +106,28 @@ struct Plan {
   int sps;  // super-blocks per split
 };
 
+// Workspace of a K split: one arrival counter per output tile in a fixed
+// region at the start (zero between calls, whatever the shape, so one
+// workspace serves calls of different shapes), then the S partial slices
+// [S][M][ldp] f32 with the row stride ldp = N rounded up to 64 (whole
+// 256-byte segments per tile row; read through 32-bit offsets, so below
+// 2 GiB).
+constexpr int64_t kCounterBytes = 65536;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+int64_t split_ld(int64_t N) { return (N + 63) / 64 * 64; }
+
 // The plan of a given configuration and K split (S is reduced to the
-// number of non-empty splits).
+// number of non-empty splits; no split where the output has more tiles than
+// the workspace has counters).
 Plan make_plan(int cfg, int S, int64_t N, int64_t K, int64_t M) {
   const int64_t SB = K / 256;
   const int64_t sps = cdiv(SB, S);
   const int max_tb = qgemm_cfg_max_tb(cfg);
   const int tb = tb_for(M) < max_tb ? tb_for(M) : max_tb;
-  return Plan{tb, cfg, cdiv(N, qgemm_cfg_rows(cfg)), cdiv(M, (int64_t)16 * tb), (int)cdiv(SB, sps), (int)sps};
+  const int64_t n_tiles = cdiv(N, qgemm_cfg_rows(cfg)), m_tiles = cdiv(M, (int64_t)16 * tb);
+  if (n_tiles * m_tiles > kMaxSplitTiles || (int64_t)S * M * split_ld(N) * 4 >= ((int64_t)1 << 31))
+    return Plan{tb, cfg, n_tiles, m_tiles, 1, (int)SB};
+  return Plan{tb, cfg, n_tiles, m_tiles, (int)cdiv(SB, sps), (int)sps};
 }
 
 // Time of one super-block step of a work-group with a full token tile, per
@@ -151,8 +166,8 @@ constexpr Tuned kTuned[] = {
 
 // Pick the tile configuration and the K split that minimise an estimate of
 // the makespan: work-group rounds over the CUs times super-blocks per
-// work-group times the step time, plus, for a split, the reduction (~2.4 us
-// and ~0.54 us per MB of partials).  With no workspace, S = 1.
+// work-group times the step time, plus, for a split, the reduction at the
+// end of the kernel (~1 us and ~0.54 us per MB of partials).  With no workspace, S = 1.
 Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   Plan best{};
   double best_cost = 1e300;
@@ -166,8 +181,6 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
     for (int64_t S = 1; S <= smax; ++S) {
       const Plan pl = make_plan(cfg, (int)S, N, K, M);
       if (pl.S != S) continue;
-      // the reduction reads the partials through 32-bit buffer offsets
-      if (S > 1 && (S + 3) * M * N * 4 >= ((int64_t)1 << 32)) break;
       const int max_tb = qgemm_cfg_max_tb(cfg);
       // per-step time scales roughly with the tokens per work-group
       const double step_us = kCfgStepUs[cfg] * (qtype == 14 ? kCfgQ6Factor[cfg] : 1.0) *
@@ -175,7 +188,7 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
       const int64_t wgs = pl.n_tiles * pl.m_tiles * S;
       const int64_t rounds = cdiv(wgs, kCUs);
       double cost = (double)rounds * (double)pl.sps * step_us;
-      if (S > 1) cost += 2.4 + (double)S * (double)M * (double)N * 4.0 * 0.54e-6;
+      if (S > 1) cost += 1.0 + (double)S * (double)M * (double)N * 4.0 * 0.54e-6;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = pl;
@@ -185,38 +198,38 @@ Plan plan_gemm(int qtype, int64_t N, int64_t K, int64_t M, bool allow_split) {
   return best;
 }
 
-// Launch a planned GEMM: y directly, or split partials in the workspace and
-// their reduction.
+int64_t split_workspace_bytes(const Plan& pl, int64_t M, int64_t N) {
+  return pl.S > 1 ? kCounterBytes + (int64_t)pl.S * M * split_ld(N) * 4 : 0;
+}
+
+// Launch a planned GEMM: y directly, or the split partials in the workspace
+// with their reduction fused into the same kernel.
 int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
              const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
              hipStream_t s) {
-  GemmParams p;
+  GemmParams p{};
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
   p.dmax = x_dmax;
-  p.keys = nullptr;
-  p.stats = nullptr;
   p.N = N;
   p.SB = K / 256;
   p.M = M;
   p.sps = pl.sps;
   const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
-  auto launch = [&]() { return launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s); };
-  int rc;
   if (pl.S == 1) {
     p.out = y;
     p.ldo = ldy;
-    p.split_stride = 0;
     p.bias = bias;
-    if ((rc = hip_status(launch(), fn))) return rc;
-    return ok();
+  } else {
+    p.out = (float*)((uint8_t*)workspace + kCounterBytes);
+    p.ldo = split_ld(N);
+    p.split_stride = M * p.ldo;
+    p.tile_cnt = (uint32_t*)workspace;
+    p.red_y = y;
+    p.red_ldy = ldy;
+    p.red_bias = bias;  // added once, by the reduction
   }
-  p.out = (float*)workspace;
-  p.ldo = N;
-  p.split_stride = M * N;
-  p.bias = nullptr;  // the reduction adds it once
-  if ((rc = hip_status(launch(), fn))) return rc;
-  return hip_status(launch_split_reduce((const float*)workspace, pl.S, M, N, y, ldy, bias, s), fn);
+  return hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn);
 }
 
 }  // namespace
@@ -311,8 +324,7 @@ int dllm_decode_qk(int qtype, const void* w, int64_t n_superblocks, void* out, v
 
 int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M) {
   if (check_qtype(qtype) || N <= 0 || M <= 0 || K <= 0 || K % 256) return -1;
-  const Plan p = plan_gemm(qtype, N, K, M, true);
-  return p.S > 1 ? (int64_t)p.S * M * N * 4 : 0;
+  return split_workspace_bytes(plan_gemm(qtype, N, K, M, true), M, N);
 }
 
 static int check_gemm_args(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const void* xq, int64_t M) {
@@ -340,7 +352,7 @@ static int qgemm_impl(const char* fn, int qtype, const void* w, int64_t N, int64
   if (!aligned(y, 4) || !aligned(x_dmax, 4) || !aligned(bias, 4))
     return fail(DLLM_E_ALIGN, "%s: y, x_dmax and bias must be 4-byte aligned", fn);
   Plan pl = plan_gemm(qtype, N, K, M, true);
-  const int64_t need = pl.S > 1 ? (int64_t)pl.S * M * N * 4 : 0;
+  const int64_t need = split_workspace_bytes(pl, M, N);
   if (pl.S > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     pl = plan_gemm(qtype, N, K, M, false);  // no usable workspace: whole K range per work-group
   return run_plan(fn, qtype, pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, (hipStream_t)stream);
@@ -359,7 +371,6 @@ int dllm_qgemm_bias(int qtype, const void* w, int64_t N, int64_t K, const void* 
                     stream);
 }
 
-static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Key slots per gathered row: one per 64-row tile (tiled path) or one per
 // wave (streaming path), whichever is more.
@@ -435,7 +446,7 @@ static int lmhead_impl(const char* fn, int qtype, const void* w, int64_t N, int6
     return hip_status(launch_argmax_finalize(keys, stats, lmhead_stream_slots(N), n_rows, argmax, lse, p_max, s),
                       "lm head argmax launch");
   }
-  GemmParams p;
+  GemmParams p{};
   p.w = (const uint8_t*)w;
   p.xq = xq;
   p.dmax = nullptr;
@@ -501,10 +512,7 @@ int dllm_qgemm_planned(int qtype, const void* w, int64_t N, int64_t K, const voi
   if (split < 1 || split > K / 256) return fail(DLLM_E_ARG, "%s: split=%d must be in [1, K/256]", fn, split);
   const Plan pl = make_plan(tile, split, N, K, M);
   if (pl.S > 1) {
-    if ((pl.S + 3) * M * N * 4 >= ((int64_t)1 << 32))
-      return fail(DLLM_E_SHAPE, "%s: %d partial slices of %lld x %lld are too large", fn, pl.S, (long long)M,
-                  (long long)N);
-    const int64_t need = (int64_t)pl.S * M * N * 4;
+    const int64_t need = split_workspace_bytes(pl, M, N);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
       return fail(DLLM_E_WORKSPACE, "%s: split %d needs a 16-byte aligned workspace of %lld bytes", fn, pl.S,
                   (long long)need);
@@ -533,7 +541,7 @@ int dllm_qgemm_superblock_sums_i32(int qtype, const void* w, int64_t N, int64_t 
   Plan pl = make_plan(tile, split, N, K, M);
   pl.tb = qgemm_cfg_max_tb(tile);
   pl.m_tiles = cdiv(M, (int64_t)16 * pl.tb);
-  GemmParams p;
+  GemmParams p{};
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
   p.dmax = nullptr;

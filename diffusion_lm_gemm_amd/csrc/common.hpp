@@ -51,6 +51,20 @@ __device__ __forceinline__ v2u buf_ld64(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ v4u buf_ld128(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// Device-coherent 16-byte load and store (cache policy sc1: coherent across
+// the XCDs, whose L2 caches are not coherent with each other; the store
+// writes through to memory).  For data that one work-group writes and a work
+// group on another XCD reads in the same kernel.
+constexpr int kCoherentAux = 16;  // sc1
+__device__ __forceinline__ v4u buf_ld128_dev(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherentAux);
+}
+__device__ __forceinline__ void buf_st128_dev(rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCoherentAux);
+}
+// Wait until every memory access this wave issued has completed (vmcnt 0;
+// expcnt and lgkmcnt left alone).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Eight bytes at a 2-byte aligned offset, from dword-aligned loads of only
 // the dwords that hold them.
 __device__ __forceinline__ void buf_ld64_a2(rsrc_t r, uint32_t off, uint32_t& x0, uint32_t& x1) {

@@ -18,6 +18,14 @@ struct GemmParams {
   int64_t ldo;           // leading dimension of out
   int64_t split_stride;  // floats between split slices of out
   int sps;               // super-blocks per split
+  // K split with its reduction fused (tile_cnt not null): out holds the
+  // split slices; the last of a tile's split work-groups to finish sums them
+  // in split order, adds red_bias (or nothing), writes red_y, and resets the
+  // tile's arrival counter tile_cnt[blockIdx.z * gridDim.x + blockIdx.x] to 0
+  uint32_t* tile_cnt;
+  float* red_y;
+  int64_t red_ldy;
+  const float* red_bias;
 };
 
 // Streaming LM head: at most 32 gathered Q8_K rows (xq, [M][SB] records)
@@ -59,9 +67,6 @@ hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 gr
 // The same kernels in their test form: the exact int32 super-block sums
 // A[m][n][sb] go to p.out instead of y; token tile qgemm_cfg_max_tb(cfg).
 hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s);
-// y = the sum of the S partial slices, plus bias[n] per column when bias is not null.
-hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
-                               hipStream_t s);
 bool lmhead_stream_fits(int64_t K, int64_t n_rows);
 int lmhead_stream_waves();             // the most waves (key slots per row) it uses
 int64_t lmhead_stream_slots(int64_t N);  // the waves it uses for N rows

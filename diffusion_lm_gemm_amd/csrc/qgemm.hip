@@ -24,11 +24,15 @@
 //    power of two so the f16 halves cannot overflow; the output is scaled back
 //    exactly at the end.
 //
-// Work-group: 256 threads = 4 waves, 64 weight rows (16 per wave) x up to 160
-// tokens (TB blocks of 16).  Activations of one super-block are staged in LDS
-// and shared by the 4 waves; each wave unpacks only its own 16 rows.  K may be
-// split across work-groups (grid.y); partial tiles then go to a workspace and a
-// second kernel sums them in split order.
+// Work-group: NW = 4, 8 or 12 waves, each with RB = 1 or 2 blocks of 16
+// weight rows, x up to 160 tokens (TB blocks of 16); the seven tile
+// configurations are listed at launch_cfg.  Activations of one super-block are
+// staged in LDS and shared by the waves; each wave unpacks only its own rows.
+// The weight side of the minimum term, -dmin * m, is exact as two f16 halves
+// for every f16 dmin up to 65504/63 (a 6-bit m times an 11-bit significand
+// whose lowest bit is at least 2^-24, subnormals included).  K may be split across work-groups (grid.y): each writes its
+// partial tile to a workspace slice, and the last of a tile's work-groups to
+// finish sums the slices in split order (no second kernel).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "unpack.hpp"
@@ -46,6 +50,80 @@ namespace dllm {
 // ST = 1: one stage, loaded at the start of each step (two barriers per
 // step); with 4 waves this fits two work-groups per CU whose waits the other
 // one's work fills.
+// The K-split sum of one output tile (rows row_base .. + ROWS, tokens m0 ..
+// + TOK, clipped to N and M) in split order, plus the bias per row: slices
+// [S][M][ldo] f32 at p.out (ldo = p.ldo, a multiple of 64) -> p.red_y.
+// Deterministic and the same for every tile: acc = ((0 + P_0) + P_1) + ...,
+// then + bias.  The slices are read device-coherently (other work-groups, on
+// other XCDs, wrote them in this kernel).  y takes 16-byte stores where the
+// group of four rows lies inside N and y's rows allow it.
+template <int ROWS, int TOK, int NTH>
+__device__ __forceinline__ void sum_split_tile(const GemmParams& p, int64_t row_base, int64_t m0, int S, int tid) {
+  constexpr uint32_t kNone = 0x80000000u;  // an offset past the slices: reads zeros, no memory access
+  const int64_t N = p.N, M = p.M, ldo = p.ldo;
+  const rsrc_t wsr = make_rsrc(p.out, (int64_t)S * M * ldo * 4);
+  const uint32_t slice = (uint32_t)(M * ldo * 4);
+  float* y = p.red_y;
+  const float* bias = p.red_bias;
+  const bool yvec = (p.red_ldy % 4 == 0) && ((((uintptr_t)y) & 15) == 0);
+  // each thread owns KI groups of four rows; their loads for SB slices at a
+  // time are all in flight together
+  constexpr int G = ROWS / 4, ITEMS = TOK * G, KI = (ITEMS + NTH - 1) / NTH;
+  constexpr int SBAT = KI <= 5 ? 4 : 2;
+  int64_t mk[KI], nk[KI];
+  bool ok[KI];
+  uint32_t ek[KI];
+  v4f acc[KI];
+#pragma unroll
+  for (int k = 0; k < KI; ++k) {
+    const int idx = tid + k * NTH;
+    const int t = idx / G, g = idx - t * G;
+    mk[k] = m0 + t;
+    nk[k] = row_base + 4 * g;
+    ok[k] = idx < ITEMS && mk[k] < M && nk[k] < N;
+    ek[k] = ok[k] ? (uint32_t)((mk[k] * ldo + nk[k]) * 4) : 0u;
+    acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s = 0; s < S; s += SBAT) {
+    v4u v[SBAT][KI];
+#pragma unroll
+    for (int j = 0; j < SBAT; ++j)
+#pragma unroll
+      for (int k = 0; k < KI; ++k)
+        v[j][k] = buf_ld128_dev(wsr, (ok[k] && s + j < S) ? ek[k] + (uint32_t)(s + j) * slice : kNone);
+    // in split order; a slice past S adds +0, which leaves the sum unchanged
+#pragma unroll
+    for (int j = 0; j < SBAT; ++j)
+#pragma unroll
+      for (int k = 0; k < KI; ++k) acc[k] += __builtin_bit_cast(v4f, v[j][k]);
+  }
+#pragma unroll
+  for (int k = 0; k < KI; ++k) {
+    if (!ok[k]) continue;
+    const int64_t m = mk[k], n = nk[k];
+    float* dst = y + m * p.red_ldy + n;
+    v4f a = acc[k];
+    if (n + 3 < N) {
+      if (bias) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] += bias[n + i];
+      }
+      if (yvec) {
+        __builtin_nontemporal_store(a, (v4f*)dst);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = a[i];
+      }
+    } else {
+      for (int i = 0; i < 4 && n + i < N; ++i) dst[i] = bias ? a[i] + bias[n + i] : a[i];
+    }
+  }
+}
+
+// A buffer offset past every operand (they stay below 2 GiB): a load there
+// reads zeros and makes no memory access.
+constexpr uint32_t kNoLoad = 0x80000000u;
+
 // SUMS: the test form of the same kernel, which also stores every tile's
 // exact int32 super-block sums A_sb = (hi << shift) + lo, as formed for the
 // epilogue, to ((int32_t*)p.out)[(m * N + n) * SB + sb], and writes no y.
@@ -380,7 +458,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     const bool more = sb + 1 < s1;
     act_dma(act_next, sb + 1);  // past the end: an unread stage
     items_load(sb + 1);
-    const uint32_t noff = wrow_off[0] + (uint32_t)((sb + 1) * BYTES);  // the next block
+    // the block after next, which raw is refilled with once the next one is
+    // unpacked; past the split's end an offset beyond the buffer, which reads
+    // zeros without touching memory (the load is issued either way, so the
+    // waits stay the same on every path)
+    const uint32_t noff = (sb + 2 < s1) ? wrow_off[0] + (uint32_t)((sb + 2) * BYTES) : kNoLoad;
     uint32_t sc03 = 0u, sc47 = 0u, mn03, mn47;
     if constexpr (MINS) {
       q4k_scales(raw[0][1], raw[0][2], raw[0][3], sc03, sc47, mn03, mn47);
@@ -439,7 +521,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if ((c * TB) / 4 == t) unpack_chunk<QT>(raw[0], g4, c, sc03, sc47, An.lo[c], An.hi[c]);
-      if (t == (3 * TB) / 4) load_raw<QT>(wr, noff + BYTES, g4, raw[0]);
+      if (t == (3 * TB) / 4) load_raw<QT>(wr, noff, g4, raw[0]);
       if (t == TB - 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) An.dsel[i] = __shfl(dnext, 4 * g4 + i);
@@ -484,7 +566,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       mh2[0] = mine ? mhn2 : mh2[0];
       mh3[0] = mine ? mhn3 : mh3[0];
     }
-    items_store(buf ^ 1, (it + 1) & 7);
+    items_store(buf ^ 1, (it + 1) & 7);  // past the end: an unread stage
     __syncthreads();
   };
 
@@ -496,6 +578,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     act_dma(s_act0, s0);
     items_load(s0);
   }
+
 
   // Per-token power-of-two pre-scale of d_x (Q4_K: keeps the f16 halves of
   // d_x * S_j in range; undone exactly at the end); 1 for Q6_K.  It comes
@@ -548,7 +631,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       mh2[0] = mine ? raw[0][2] : 0u;
       mh3[0] = mine ? raw[0][3] : 0u;
     }
-    load_raw<QT>(wr, wrow_off[0] + (uint32_t)((s0 + 1) * BYTES), g4, raw[0]);
+    load_raw<QT>(wr, s0 + 1 < s1 ? wrow_off[0] + (uint32_t)((s0 + 1) * BYTES) : kNoLoad, g4, raw[0]);
     int64_t sb = s0;
     for (; sb + 1 < s1; sb += 2) {
       step_pp(sb, s_act0, s_act1, 0, A0, A1);
@@ -569,6 +652,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // reduction adds it instead)
   if constexpr (SUMS) return;
   float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
+  // K split with the reduction fused: the slice [M][ldo] goes out with
+  // device-coherent 16-byte stores (ldo a multiple of 64 >= N, so every
+  // group of four rows that starts inside N is whole)
+  const rsrc_t wsr = make_rsrc(p.out, p.tile_cnt ? (int64_t)gridDim.y * p.split_stride * 4 : 0);
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int64_t nbase = row0 + 16 * b + 4 * g4;
@@ -584,7 +671,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       const float inv = 1.0f / s_esc[t * 16 + r];  // exact: a power of two
       const v4f yv = p.bias ? yacc[b][t] * inv + bv : yacc[b][t] * inv;
       yacc[b][t] = yv;
-      if (m < M) {
+      if (p.tile_cnt) {
+        if (m < M && nbase < N)
+          buf_st128_dev(wsr, (uint32_t)(((int64_t)blockIdx.y * p.split_stride + m * p.ldo + nbase) * 4),
+                        __builtin_bit_cast(v4u, yv));
+      } else if (m < M) {
         float* dst = outp + m * p.ldo + nbase;
         if (nbase + 3 < N && ((((uintptr_t)dst) & 15) == 0)) {
           // streamed out (non-temporal): the readers of y or of the split
@@ -598,6 +689,28 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
         }
       }
     }
+  }
+
+  if (p.tile_cnt) {
+    // K split with the reduction fused: once this work-group's slice has
+    // reached memory (each wave waits for its own stores), it is counted in
+    // with a device-scope atomic; the last of the tile's gridDim.y
+    // work-groups to arrive sums the slices.  That last arrival also resets
+    // the counter, so the next call on the stream finds it 0.  The slices
+    // are written and read with device-coherent accesses, so no cache
+    // maintenance is needed on either side.
+    __shared__ int s_last;
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t* c = p.tile_cnt + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+      const uint32_t before = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = (before + 1 == gridDim.y);
+      if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_last) sum_split_tile<ROWS, TOK, NTH>(p, (int64_t)blockIdx.x * ROWS, m0, (int)gridDim.y, tid);
   }
 
   if constexpr (ARGMAX) {
@@ -648,64 +761,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
         for (int k = 1; k < NW; ++k) softmax_merge(sm, ss, s_stat[k * TOK + tid].x, s_stat[k * TOK + tid].y);
         if (m < M) p.stats[(int64_t)blockIdx.x * M + m] = float2{sm, ss};
       }
-    }
-  }
-}
-
-// Sum of the K-split partial tiles in split order (deterministic): each
-// thread owns four consecutive elements of the M x N partial tile.  The
-// slices are read through a buffer resource, so elements past M x N read as
-// zero.  SC > 0 fixes the number of slices at compile time, so that all of a
-// thread's loads are in flight together; SC == 0 takes S at run time, four
-// slices at a time.  VEC: the four elements are one 16-byte store (N and ldy
-// multiples of four, y and bias 16-byte aligned); otherwise element stores,
-// which also handle a row change inside the four.  A bias (f32 per column,
-// or null) is added to the sum once.
-template <int SC, bool VEC>
-__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int S, int64_t M,
-                                                    int64_t N, float* __restrict__ y, int64_t ldy,
-                                                    const float* __restrict__ bias) {
-  if constexpr (SC > 0) S = SC;
-  const int64_t MN = M * N;
-  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e0 >= MN) return;
-  const rsrc_t r = make_rsrc(ws, (int64_t)S * MN * 4);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  if (VEC || e0 + 4 <= MN) {
-    if constexpr (SC > 0) {
-      v4u v[SC];
-#pragma unroll
-      for (int u = 0; u < SC; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)u * MN + e0) * 4));
-#pragma unroll
-      for (int u = 0; u < SC; ++u) acc += __builtin_bit_cast(v4f, v[u]);
-    } else {
-      int s0 = 0;
-      for (; s0 + 4 <= S; s0 += 4) {
-        v4u v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = buf_ld128(r, (uint32_t)(((int64_t)(s0 + u) * MN + e0) * 4));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc += __builtin_bit_cast(v4f, v[u]);
-      }
-      for (; s0 < S; ++s0) acc += __builtin_bit_cast(v4f, buf_ld128(r, (uint32_t)(((int64_t)s0 * MN + e0) * 4)));
-    }
-  } else {
-    // the last, partial group of four: element loads (a 16-byte load that
-    // reaches past the end of the range would read as zero whole)
-    for (int s0 = 0; s0 < S; ++s0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] += __builtin_bit_cast(float, buf_ld32(r, (uint32_t)(((int64_t)s0 * MN + e0 + i) * 4)));
-  }
-  int64_t m = e0 / N, n = e0 - m * N;
-  if constexpr (VEC) {
-    if (bias) acc += *(const v4f*)(bias + n);
-    __builtin_nontemporal_store(acc, (v4f*)(y + m * ldy + n));  // streamed out, as the GEMM's own stores
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (e0 + i < MN) y[m * ldy + n] = bias ? acc[i] + bias[n] : acc[i];
-      if (++n == N) { n = 0; ++m; }
     }
   }
 }
@@ -875,30 +930,6 @@ int qgemm_cfg_max_tb(int cfg) { return (cfg == 3 || cfg == 4 || cfg == 6 || cfg 
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_cfg<QT_Q4K>(p, tb, cfg, grid, argmax, s);
   return launch_cfg<QT_Q6K>(p, tb, cfg, grid, argmax, s);
-}
-
-template <bool VEC>
-static void launch_reduce_s(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
-                            hipStream_t s) {
-  const dim3 grid((unsigned)((M * N + 1023) / 1024)), block(256);
-  switch (S) {
-    case 2: hipLaunchKernelGGL((k_split_reduce<2, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-    case 3: hipLaunchKernelGGL((k_split_reduce<3, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-    case 4: hipLaunchKernelGGL((k_split_reduce<4, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-    case 6: hipLaunchKernelGGL((k_split_reduce<6, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-    case 8: hipLaunchKernelGGL((k_split_reduce<8, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-    default: hipLaunchKernelGGL((k_split_reduce<0, VEC>), grid, block, 0, s, ws, S, M, N, y, ldy, bias); break;
-  }
-}
-
-hipError_t launch_split_reduce(const float* ws, int S, int64_t M, int64_t N, float* y, int64_t ldy, const float* bias,
-                               hipStream_t s) {
-  const bool vec = (N % 4 == 0) && (ldy % 4 == 0) && ((((uintptr_t)y) & 15) == 0) && ((((uintptr_t)bias) & 15) == 0);
-  if (vec)
-    launch_reduce_s<true>(ws, S, M, N, y, ldy, bias, s);
-  else
-    launch_reduce_s<false>(ws, S, M, N, y, ldy, bias, s);
-  return hipGetLastError();
 }
 
 hipError_t launch_argmax_finalize(const uint64_t* keys, const float2* stats, int64_t n_tiles, int64_t M,

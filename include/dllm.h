@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 8
+#define DLLM_ABI_VERSION 9
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -156,9 +156,17 @@ int dllm_decode_qk(int qtype, const void *w, int64_t n_superblocks,
  *   y       f32 [M][ldy], ldy >= N, 4-byte aligned (written, not accumulated)
  *   workspace / workspace_bytes   optional scratch for splitting K across
  *           work-groups; NULL/0 runs without a split.  A split needs
- *           dllm_qgemm_workspace_bytes(qtype, N, K, M) bytes; with less the
- *           call runs without a split.  The result agrees with the exact
- *           dequantized product to f32 rounding either way.
+ *           dllm_qgemm_workspace_bytes(qtype, N, K, M) bytes, 16-byte
+ *           aligned; with less the call runs without a split.  Its first
+ *           64 KiB hold one arrival counter per output tile, the split's
+ *           partial tiles follow: the last of a tile's work-groups to finish
+ *           sums the partials in split order (in the same kernel) and sets
+ *           the counter back to 0.  So the workspace must be zero-filled once
+ *           before its first use, and every call leaves it ready for the next
+ *           one, of any shape; calls that share a workspace must be ordered
+ *           on one stream.  The result
+ *           agrees with the exact dequantized product to f32 rounding either
+ *           way, and is the same bits on every call.
  */
 int64_t dllm_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M);
 int dllm_qgemm(int qtype, const void *w, int64_t N, int64_t K,
@@ -267,8 +275,10 @@ int dllm_qgemm_superblock_sums_i32(int qtype, const void *w, int64_t N,
  * dllm_qgemm_planned: dllm_qgemm_bias with a given tile configuration and K
  *   split: tile 1..7 (the work-group shapes of the 16 x 16 tiles); split in
  *   [1, K/256] (reduced to the number of non-empty splits).  A split S > 1
- *   needs a 16-byte aligned workspace of S * M * N * 4 bytes (DLLM_E_WORKSPACE
- *   otherwise).  The result agrees with dllm_qgemm to f32 rounding.
+ *   needs a 16-byte aligned, zero-filled workspace (dllm_qgemm's rules) of
+ *   65536 + S * M * N64 * 4 bytes, N64 = N rounded up to a multiple of 64
+ *   (DLLM_E_WORKSPACE otherwise).  The result agrees with dllm_qgemm to f32
+ *   rounding.
  * dllm_lmhead_planned: dllm_lmhead_confidence (lse and p_argmax may both be
  *   NULL: dllm_lmhead_masked) with path 0 (choose), 1 (the streaming kernel;
  *   K <= 4096 and n_rows <= 32, DLLM_E_SHAPE otherwise) or 2 (the tiled GEMM

@@ -132,3 +132,26 @@ def test_lmhead_strided_logits(dl, tiled):
     torch.cuda.synchronize()
     assert torch.equal(big[:, :N], ref_lg) and torch.equal(am, ref_am)
     assert torch.all(big[:, N:] == -7.0)
+
+
+def test_split_workspace_counters_return_to_zero(dl):
+    """A K-split call leaves the workspace's per-tile arrival counters (after
+    the partial slices) at zero, so that the next call -- another shape, or a
+    graph replay -- starts from a clean state; repeated calls on one
+    workspace give the same bits."""
+    M = 148
+    for qtype, N, K in [(12, 4096, 4096), (14, 4096, 12288), (12, 333, 3072)]:
+        nb = dl.qgemm_workspace_bytes(qtype, N, K, M)
+        ldp = (N + 63) // 64 * 64
+        S = (nb - 65536) // (M * ldp * 4)
+        assert S > 1 and nb == 65536 + S * M * ldp * 4, "these shapes take the K split"
+        off = 65536
+        w = _weights(qtype, N, K, 95, f"cnt-{qtype}-{N}").to(DEV)
+        xq = dl.quantize_q8k(synth.normal_f32((M, K), 95, f"cnt-x-{K}").to(DEV))
+        ws = dl.qgemm_workspace(qtype, N, K, M, DEV)
+        a = dl.qgemm(qtype, w, N, K, xq, M, workspace=ws).clone()
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:off])) == 0, f"counters of {qtype} {N}x{K}"
+        b = dl.qgemm(qtype, w, N, K, xq, M, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
