@@ -32,7 +32,7 @@ HEADER_EXPORTS = (
     "dllm_swiglu_quantize_q8k", "dllm_attention", "dllm_decode_qk",
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_qgemm_bias", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
-    "dllm_qgemm_superblock_sums_i32", "dllm_qgemm_planned", "dllm_lmhead_planned",
+    "dllm_qgemm_superblock_sums_i32", "dllm_qgemm_planned", "dllm_lmhead_planned", "dllm_qgemm_noalloc",
 )
 
 # tile configurations of dllm_qgemm_planned and the super-block sums export
@@ -69,6 +69,7 @@ def _load():
         "dllm_qgemm_superblock_sums_i32": (I, [I, P, I64, I64, P, I64, P, I, I, P]),
         "dllm_qgemm_planned": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P, I64, I, I, P]),
         "dllm_lmhead_planned": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, I, P]),
+        "dllm_qgemm_noalloc": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

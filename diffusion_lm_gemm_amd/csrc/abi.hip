@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/dllm.h"
 #include "common.hpp"
 
@@ -371,6 +373,59 @@ int dllm_qgemm_bias(int qtype, const void* w, int64_t N, int64_t K, const void* 
                     stream);
 }
 
+// ---- dllm_qgemm_noalloc: the K split in memory the library holds --------
+
+namespace {
+// The split's tile counters and partial slices (the workspace layout of
+// dllm_qgemm) in a file-scope device array: zero when the code object is
+// loaded, one copy per GPU, held until the process ends.  Every call leaves
+// the counter region zero again.  Host code only ever uses the address that
+// hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr int64_t kScratchBytes = (int64_t)24 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, set on the first call there
+
+int scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DLLM_E_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLLM_E_HIP, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DLLM_E_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLLM_OK;
+}
+}  // namespace
+
+int dllm_qgemm_noalloc(int qtype, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax,
+                       int64_t M, const float* bias, float* y, int64_t ldy, void* stream) {
+  const char* fn = "dllm_qgemm_noalloc";
+  int rc = check_gemm_args(fn, qtype, w, N, K, x_q8k, M);
+  if (rc) return rc;
+  if (!y) return fail(DLLM_E_ARG, "%s: null output pointer", fn);
+  if (ldy < N) return fail(DLLM_E_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (!aligned(y, 4) || !aligned(x_dmax, 4) || !aligned(bias, 4))
+    return fail(DLLM_E_ALIGN, "%s: y, x_dmax and bias must be 4-byte aligned", fn);
+  const Plan pl = plan_gemm(qtype, N, K, M, true);  // dllm_qgemm's plan with a large enough workspace
+  const int64_t need = split_workspace_bytes(pl, M, N);
+  if (need > kScratchBytes)
+    return fail(DLLM_E_WORKSPACE,
+                "%s: the K split of this shape (N=%lld, K=%lld, M=%lld) needs %lld bytes of scratch, more than the "
+                "%lld the library holds; call dllm_qgemm_bias with a workspace instead",
+                fn, (long long)N, (long long)K, (long long)M, (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  if (pl.S > 1 && (rc = scratch_for_current_device(fn, &ws))) return rc;
+  return run_plan(fn, qtype, pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, ws, (hipStream_t)stream);
+}
 
 // Key slots per gathered row: one per 64-row tile (tiled path) or one per
 // wave (streaming path), whichever is more.

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 9
+#define DLLM_ABI_VERSION 10
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -186,6 +186,26 @@ int dllm_qgemm_bias(int qtype, const void *w, int64_t N, int64_t K,
                     const void *x_q8k, const float *x_dmax, int64_t M,
                     const float *bias, float *y, int64_t ldy, void *workspace,
                     int64_t workspace_bytes, void *stream);
+
+/*
+ * dllm_qgemm_bias for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same result, bit for bit, as dllm_qgemm_bias with a workspace of
+ * dllm_qgemm_workspace_bytes(qtype, N, K, M) bytes, and the same plan, but
+ * the K split's partial tiles and tile counters live in 24 MiB of device
+ * memory that the library holds for the life of the process (one copy per
+ * GPU, taken when the first call on that device finds its address).  The
+ * call allocates nothing and issues no memset.  Shapes whose split would
+ * need more than 24 MiB (65536 + S * M * N64 * 4 bytes, N64 = N rounded up
+ * to 64) are rejected with DLLM_E_WORKSPACE; shapes that run unsplit use no
+ * scratch.  The stream must belong to the current device.  Every call on a
+ * GPU shares that GPU's scratch: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.
+ */
+int dllm_qgemm_noalloc(int qtype, const void *w, int64_t N, int64_t K,
+                       const void *x_q8k, const float *x_dmax, int64_t M,
+                       const float *bias, float *y, int64_t ldy,
+                       void *stream);
 
 /*
  * Masked-row LM head (Development plan, "Compute design", last bullet; README
