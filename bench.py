@@ -46,6 +46,13 @@ def parse():
     ap.add_argument("--no-dream", action="store_true", help="skip the Dream-7B-shaped step (a reported extra)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--no-l160", action="store_true", help="skip the L=160 step (a reported extra)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"), default=None,
+                    help="write profiles/OUT from the rocprofv3 --kernel-trace --stats output in DIR (libdllm "
+                         "kernels: calls, average and share per kernel and launch shape), then exit")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("TARGET", "DIR_PREFIX", "OUT"), default=None,
+                    help="write profiles/OUT from FETCH_SIZE and WRITE_SIZE passes DIR_PREFIX_FETCH_SIZE and "
+                         "DIR_PREFIX_WRITE_SIZE of a --profile-kernel TARGET run (or --profile-dominant for TARGET "
+                         "dominant), scaled by the same counters on the run's 256 MiB copy, then exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("TARGET", "DIR_PREFIX"), default=None,
                     help="write profiles/mfma_<kernel>.txt from the counter passes DIR_PREFIX_{A,B,C} of a "
                          "--profile-kernel TARGET run (rocprofv3 --pmc ... --output-format csv), then exit")
@@ -346,6 +353,12 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
         return
     if args.profile_dominant:
         profile_dominant(args)
@@ -809,6 +822,105 @@ def summarize_pmc(spec):
     path = os.path.join(ROOT, "profiles", f"mfma_{name}.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     print(f"[summarize-pmc] wrote {path}: mfma_util {fig['mfma_util']:.3f}, valu/mfma {fig['valu_per_mfma']:.2f}")
+
+
+def _short_kernel(name: str) -> str:
+    """k_qgemm<12, 5, 12, 1, false, 2, false> from a demangled or plain name."""
+    n = name.split("(")[0].replace("void ", "").replace("dllm::", "")
+    return n.strip()
+
+
+def summarize_trace(d, out):
+    """profiles/<out>: libdllm kernels of a rocprofv3 --kernel-trace run
+    (per kernel and per kernel + grid)."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
+    per, per_grid = {}, {}
+    for r in rows:
+        kn = _short_kernel(r["Kernel_Name"])
+        if not kn.startswith("k_"):
+            continue
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        wg = [int(r[f"Workgroup_Size_{a}"]) for a in "XYZ"]
+        grid = tuple(int(r[f"Grid_Size_{a}"]) // w for a, w in zip("XYZ", wg))
+        per.setdefault(kn, []).append(us)
+        per_grid.setdefault((kn, grid), []).append(us)
+    tot = sum(sum(v) for v in per.values())
+    lines = [f"# libdllm kernels of one rocprofv3 --kernel-trace --stats run; durations in microseconds",
+             f"# source: {os.path.basename(os.path.normpath(d))}/run_kernel_trace.csv; summary: "
+             f"python3 bench.py --summarize-trace <dir> {out}",
+             f"# kernel_sha={_kernel_hash()}", "",
+             f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'total_us':>11s} {'share':>6s}"]
+    for kn, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{kn:44s} {len(v):6d} {sum(v) / len(v):9.2f} {sum(v):11.1f} {100 * sum(v) / tot:5.1f}%")
+    lines += ["", f"{'kernel (grid x,y,z in work-groups)':56s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for (kn, g), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{kn + ' (' + ','.join(map(str, g)) + ')':56s} {len(v):6d} {sum(v) / len(v):9.2f} "
+                     f"{min(v):9.2f} {max(v):9.2f}")
+    path = os.path.join(ROOT, "profiles", out)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(f"[summarize-trace] wrote {path}")
+
+
+def summarize_traffic(target, prefix, out):
+    """profiles/<out>: HBM bytes per call of a target's kernel from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+    reads for the run's 256 MiB device copy."""
+    import csv
+    pick = {"lmhead": "k_lmhead", "quant4096": "k_quantize", "quant12288": "k_quantize", "rmsnorm": "k_quantize",
+            "swiglu": "k_quantize", "attention": "k_attention"}.get(target, "k_qgemm")
+    res = {}
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(f"{prefix}_{cn}", "run_counter_collection.csv"))))
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == cn]
+        kern = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows
+                if pick in r["Kernel_Name"] and r["Counter_Name"] == cn]
+        copy_bytes = 256 << 20  # read and written once by the copy
+        per_kib = copy_bytes / copy[0]
+        res[cn] = (sum(v for v, _ in kern) / len(kern), per_kib, len(kern), kern[0][1])
+    f_kib, f_scale, n, kname = res["FETCH_SIZE"]
+    w_kib, w_scale, _, _ = res["WRITE_SIZE"]
+    rd, wr = f_kib * f_scale, w_kib * w_scale
+    L = 148
+    other = {  # (what, algorithmic bytes per call) of the calls outside STEP_CALLS
+        "lmhead": ("the masked-row LM head, 32 rows x 126464 x 4096 Q6_K (streaming kernel)",
+                   VOCAB * D // 256 * 210 + MASKED * D // 256 * 292 + MASKED * VOCAB * 4),
+        "rmsnorm": (f"RMSNorm -> Q8_K, {L} x {D}", L * D * 4 + D * 4 + L * D // 256 * 292 + L * 4),
+        "swiglu": (f"SwiGLU -> Q8_K, {L} x 2 x {FFN}", L * 2 * FFN * 4 + L * FFN // 256 * 292 + L * 4),
+        "attention": (f"bidirectional attention, L={L}, 32 heads x 128 (f32 Q+K+V rows in, f32 out)",
+                      L * 3 * D * 4 + L * D * 4),
+    }
+    if target == "dominant":
+        q, N, K, what = 12, 2 * FFN, D, "gate+up Q4_K 24576x4096"
+    elif target in STEP_CALLS:
+        q, N, K, what = STEP_CALLS[target]
+    else:
+        q, (what, alg) = -1, other[target]
+    if q == -1:
+        pass
+    elif q == 0:
+        alg = L * K * 4 + L * K // 256 * 292 + L * 4
+    else:
+        alg = N * K // 256 * (144 if q == 12 else 210) + L * K // 256 * 292 + L * N * 4
+    cmd = "--profile-dominant" if target == "dominant" else f"--profile-kernel {target}"
+    lines = [f"# HBM traffic of {what} at L={L} (bench.py {cmd})",
+             f"# kernel: {_short_kernel(kname)}",
+             "# commands (each counter in its own pass; run from /tmp with TMPDIR=/tmp):",
+             f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prefix}_FETCH_SIZE -o run -- python3 bench.py {cmd} --steps 5",
+             f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prefix}_WRITE_SIZE -o run -- python3 bench.py {cmd} --steps 5",
+             f"#   python3 bench.py --summarize-traffic {target} {prefix} {out}",
+             f"# calibration: the same counters on the 256 MiB device copy the run makes first:",
+             f"#   FETCH_SIZE -> {f_scale:.2f} bytes per counted KiB, WRITE_SIZE -> {w_scale:.2f} bytes per counted KiB",
+             f"# kernel, mean of {n} dispatches: FETCH_SIZE {f_kib:.2f} KiB, WRITE_SIZE {w_kib:.2f} KiB",
+             f"# -> read {rd / 1e6:.2f} MB + written {wr / 1e6:.2f} MB per call; algorithmic bytes per call "
+             f"{alg / 1e6:.2f} MB (ratio {(rd + wr) / alg:.3f})",
+             "# kernel_sha: hash of the kernel sources the counters were taken on",
+             f"kernel_sha={_kernel_hash()}",
+             f"bytes_per_call={int(rd + wr)}", f"read_bytes_per_call={int(rd)}", f"write_bytes_per_call={int(wr)}",
+             f"algorithmic_bytes_per_call={alg}"]
+    path = os.path.join(ROOT, "profiles", out)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(f"[summarize-traffic] wrote {path}: read {rd / 1e6:.2f} MB, written {wr / 1e6:.2f} MB, alg {alg / 1e6:.2f} MB")
 
 
 def _kernel_hash() -> str:
