@@ -62,6 +62,15 @@ __device__ __forceinline__ v4u buf_ld128_dev(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_st128_dev(rsrc_t r, uint32_t off, v4u v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCoherentAux);
 }
+__device__ __forceinline__ uint32_t buf_ld32_dev(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherentAux);
+}
+__device__ __forceinline__ void buf_st32_dev(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCoherentAux);
+}
+__device__ __forceinline__ void buf_st16_dev(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCoherentAux);
+}
 // Wait until every memory access this wave issued has completed (vmcnt 0;
 // expcnt and lgkmcnt left alone).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -83,8 +92,12 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
 // top 11 significant bits of a by truncation (exact in f16 for |a| in the
 // normal f16 range), and lo is formed from exactly the bits stored in hi:
 // the compiler may lower separate f32->f16 conversions with different
-// rounding, so hi's value is pinned before it is reused.
+// rounding, so hi's value is pinned before it is reused.  a is taken as the
+// rounded f32 value the caller passes: with contraction off here, a product
+// formed by the caller is never fused into the subtraction, so every kernel
+// instantiation splits the same value the same way.
 __device__ __forceinline__ void split_f16(float a, _Float16& hi, _Float16& lo) {
+#pragma clang fp contract(off)
   const float ht = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u);
   unsigned short hb = __builtin_bit_cast(unsigned short, (_Float16)ht);
   asm volatile("" : "+v"(hb));

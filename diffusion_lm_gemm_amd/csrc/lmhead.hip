@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = (ah[i] << SHIFT) + al[i];
-        yacc[t][i] += (float)a * (dsel[i] * dx);
+        yacc[t][i] = __builtin_fmaf((float)a, dsel[i] * dx, yacc[t][i]);
       }
     }
     if constexpr (MINS) {
