@@ -33,7 +33,6 @@ HEADER_EXPORTS = (
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_qgemm_bias", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
     "dllm_qgemm_superblock_sums_i32", "dllm_qgemm_planned", "dllm_lmhead_planned", "dllm_qgemm_noalloc",
-    "dllm_quantize_qgemm_workspace_bytes", "dllm_quantize_qgemm", "dllm_quantize_qgemm_planned",
 )
 
 # tile configurations of dllm_qgemm_planned and the super-block sums export
@@ -71,9 +70,6 @@ def _load():
         "dllm_qgemm_planned": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P, I64, I, I, P]),
         "dllm_lmhead_planned": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, I, P]),
         "dllm_qgemm_noalloc": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P]),
-        "dllm_quantize_qgemm_workspace_bytes": (I64, [I, I64, I64, I64]),
-        "dllm_quantize_qgemm": (I, [I, P, I64, I64, P, I64, I64, P, P, P, P, I64, P, I64, P]),
-        "dllm_quantize_qgemm_planned": (I, [I, P, I64, I64, P, I64, I64, P, P, P, P, I64, P, I64, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -345,36 +341,3 @@ def lmhead_planned(qtype: int, w: torch.Tensor, N: int, K: int, h: torch.Tensor,
                                    _ptr(logits), logits.stride(0), _ptr(argmax), _ptr(lse), _ptr(p_am),
                                    _ptr(workspace), workspace.numel(), path, _stream(dev)))
     return logits, argmax, lse, p_am
-
-
-def quantize_qgemm_workspace(qtype: int, N: int, K: int, M: int, device) -> torch.Tensor:
-    """A zero-filled workspace for quantize_qgemm at this shape."""
-    nb = int(lib.dllm_quantize_qgemm_workspace_bytes(qtype, N, K, M))
-    return torch.zeros(nb, dtype=torch.uint8, device=device)
-
-
-def quantize_qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x: torch.Tensor, workspace: torch.Tensor,
-                   y: torch.Tensor | None = None, x_q8k: torch.Tensor | None = None,
-                   x_dmax: torch.Tensor | None = None, bias: torch.Tensor | None = None,
-                   tile: int = 0, split: int = 1):
-    """Quantize x (f32 [M, K], row stride ldx) and multiply in one launch:
-    (y, x_q8k, x_dmax).  tile > 0 picks the tile configuration and K split
-    (test entry)."""
-    dev = _dev(w)
-    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
-    M = x.shape[0]
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    if x_q8k is None:
-        x_q8k = torch.empty((M, K // QK_K * 292), dtype=torch.uint8, device=dev)
-    if x_dmax is None:
-        x_dmax = torch.empty(M, dtype=torch.float32, device=dev)
-    assert y.dtype == torch.float32 and y.stride(1) == 1
-    wsb = workspace.numel() * workspace.element_size()
-    args = (qtype, _ptr(w), N, K, _ptr(x), x.stride(0), M, _ptr(bias), _ptr(x_q8k), _ptr(x_dmax), _ptr(y),
-            y.stride(0), _ptr(workspace), wsb)
-    if tile:
-        _check(lib.dllm_quantize_qgemm_planned(*args, tile, split, _stream(dev)))
-    else:
-        _check(lib.dllm_quantize_qgemm(*args, _stream(dev)))
-    return y, x_q8k, x_dmax

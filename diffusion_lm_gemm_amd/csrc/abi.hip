@@ -114,13 +114,8 @@ struct Plan {
 // [S][M][ldp] f32 with the row stride ldp = N rounded up to 64 (whole
 // 256-byte segments per tile row; read through 32-bit offsets, so below
 // 2 GiB).
-// The counter region: split tile counters in its first 48 KiB, then for the
-// quantize-fused form a ready and a done counter per token tile (1024 each)
-// and an error word.
 constexpr int64_t kCounterBytes = 65536;
-constexpr int64_t kMaxSplitTiles = 12288;
-constexpr int64_t kFqReadyOff = 49152, kFqDoneOff = 53248, kFqErrOff = 57344;
-constexpr int64_t kFqMaxTokenTiles = 1024;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
 int64_t split_ld(int64_t N) { return (N + 63) / 64 * 64; }
 
 // The plan of a given configuration and K split (S is reduced to the
@@ -210,16 +205,10 @@ int64_t split_workspace_bytes(const Plan& pl, int64_t M, int64_t N) {
 }
 
 // Launch a planned GEMM: y directly, or the split partials in the workspace
-// with their reduction fused into the same kernel.  With fq_x, the FQ form:
-// the quantization of fq_x into x_q8k / x_dmax fused in front (token tile
-// at the configuration's largest).
-int run_plan(const char* fn, int qtype, Plan pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
+// with their reduction fused into the same kernel.
+int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
              const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
-             hipStream_t s, const float* fq_x = nullptr, int64_t fq_ldx = 0) {
-  if (fq_x) {
-    pl.tb = qgemm_cfg_max_tb(pl.cfg);
-    pl.m_tiles = cdiv(M, (int64_t)16 * pl.tb);
-  }
+             hipStream_t s) {
   GemmParams p{};
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
@@ -241,18 +230,6 @@ int run_plan(const char* fn, int qtype, Plan pl, const void* w, int64_t N, int64
     p.red_y = y;
     p.red_ldy = ldy;
     p.red_bias = bias;  // added once, by the reduction
-  }
-  if (fq_x) {
-    p.fq_x = fq_x;
-    p.fq_ldx = fq_ldx;
-    p.fq_prod = (int)M;
-    p.fq_gx = (int)pl.n_tiles;
-    p.fq_gy = pl.S;
-    p.fq_ready = (uint32_t*)((uint8_t*)workspace + kFqReadyOff);
-    p.fq_done = (uint32_t*)((uint8_t*)workspace + kFqDoneOff);
-    p.fq_err = (uint32_t*)((uint8_t*)workspace + kFqErrOff);
-    const int64_t n_wgs = M + pl.n_tiles * pl.S * pl.m_tiles;
-    return hip_status(launch_qgemm_fq(qtype, p, pl.cfg, (unsigned)n_wgs, s), fn);
   }
   return hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn);
 }
@@ -394,66 +371,6 @@ int dllm_qgemm_bias(int qtype, const void* w, int64_t N, int64_t K, const void* 
                     void* stream) {
   return qgemm_impl("dllm_qgemm_bias", qtype, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, workspace_bytes,
                     stream);
-}
-
-// ---- quantize and GEMM in one launch ---------------------------------------
-
-int64_t dllm_quantize_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K, int64_t M) {
-  if (check_qtype(qtype) || N <= 0 || M <= 0 || K <= 0 || K % 256) return -1;
-  const int64_t split = split_workspace_bytes(plan_gemm(qtype, N, K, M, true), M, N);
-  return split > kCounterBytes ? split : kCounterBytes;
-}
-
-static int quantize_qgemm_impl(const char* fn, int qtype, const void* w, int64_t N, int64_t K, const float* x,
-                               int64_t ldx, int64_t M, const float* bias, void* x_q8k, float* x_dmax, float* y,
-                               int64_t ldy, void* workspace, int64_t workspace_bytes, int tile, int split,
-                               void* stream) {
-  int rc = check_gemm_args(fn, qtype, w, N, K, x_q8k, M);
-  if (rc) return rc;
-  if (!x || !x_dmax || !y || !workspace)
-    return fail(DLLM_E_ARG, "%s: null pointer (x=%p, x_dmax=%p, y=%p, workspace=%p)", fn, (const void*)x,
-                (void*)x_dmax, (void*)y, workspace);
-  if (ldx < K) return fail(DLLM_E_ARG, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
-  if (ldy < N) return fail(DLLM_E_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
-  if (M * ldx * 4 >= ((int64_t)1 << 31)) return fail(DLLM_E_SHAPE, "%s: x is larger than 2 GiB", fn);
-  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(x_dmax, 4) || !aligned(bias, 4) || !aligned(x_q8k, 4))
-    return fail(DLLM_E_ALIGN, "%s: x, x_q8k, x_dmax, y and bias must be 4-byte aligned", fn);
-  if (!aligned(workspace, 16)) return fail(DLLM_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  if (workspace_bytes < kCounterBytes)
-    return fail(DLLM_E_WORKSPACE, "%s: workspace of %lld bytes, need at least %lld", fn,
-                (long long)workspace_bytes, (long long)kCounterBytes);
-  Plan pl;
-  if (tile == 0) {
-    pl = plan_gemm(qtype, N, K, M, true);
-    if (pl.S > 1 && workspace_bytes < split_workspace_bytes(pl, M, N))
-      pl = plan_gemm(qtype, N, K, M, false);  // the split does not fit: whole K range per work-group
-  } else {
-    if (tile < 1 || tile > 7) return fail(DLLM_E_ARG, "%s: tile=%d must be 1..7", fn, tile);
-    if (split < 1 || split > K / 256) return fail(DLLM_E_ARG, "%s: split=%d must be in [1, K/256]", fn, split);
-    pl = make_plan(tile, split, N, K, M);
-    if (pl.S > 1 && workspace_bytes < split_workspace_bytes(pl, M, N))
-      return fail(DLLM_E_WORKSPACE, "%s: split %d needs a workspace of %lld bytes", fn, pl.S,
-                  (long long)split_workspace_bytes(pl, M, N));
-  }
-  if (cdiv(M, (int64_t)16 * qgemm_cfg_max_tb(pl.cfg)) > kFqMaxTokenTiles)
-    return fail(DLLM_E_SHAPE, "%s: M=%lld makes more than %lld token tiles", fn, (long long)M,
-                (long long)kFqMaxTokenTiles);
-  return run_plan(fn, qtype, pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, (hipStream_t)stream, x, ldx);
-}
-
-int dllm_quantize_qgemm(int qtype, const void* w, int64_t N, int64_t K, const float* x, int64_t ldx, int64_t M,
-                        const float* bias, void* x_q8k, float* x_dmax, float* y, int64_t ldy, void* workspace,
-                        int64_t workspace_bytes, void* stream) {
-  return quantize_qgemm_impl("dllm_quantize_qgemm", qtype, w, N, K, x, ldx, M, bias, x_q8k, x_dmax, y, ldy,
-                             workspace, workspace_bytes, 0, 0, stream);
-}
-
-int dllm_quantize_qgemm_planned(int qtype, const void* w, int64_t N, int64_t K, const float* x, int64_t ldx,
-                                int64_t M, const float* bias, void* x_q8k, float* x_dmax, float* y, int64_t ldy,
-                                void* workspace, int64_t workspace_bytes, int tile, int split, void* stream) {
-  if (tile == 0) return fail(DLLM_E_ARG, "dllm_quantize_qgemm_planned: tile=0 must be 1..7");
-  return quantize_qgemm_impl("dllm_quantize_qgemm_planned", qtype, w, N, K, x, ldx, M, bias, x_q8k, x_dmax, y, ldy,
-                             workspace, workspace_bytes, tile, split, stream);
 }
 
 // ---- dllm_qgemm_noalloc: the K split in memory the library holds --------

@@ -62,15 +62,6 @@ __device__ __forceinline__ v4u buf_ld128_dev(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_st128_dev(rsrc_t r, uint32_t off, v4u v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCoherentAux);
 }
-__device__ __forceinline__ uint32_t buf_ld32_dev(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherentAux);
-}
-__device__ __forceinline__ void buf_st32_dev(rsrc_t r, uint32_t off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCoherentAux);
-}
-__device__ __forceinline__ void buf_st16_dev(rsrc_t r, uint32_t off, uint16_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kCoherentAux);
-}
 // Wait until every memory access this wave issued has completed (vmcnt 0;
 // expcnt and lgkmcnt left alone).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

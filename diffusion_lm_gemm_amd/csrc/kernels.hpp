@@ -26,21 +26,6 @@ struct GemmParams {
   float* red_y;
   int64_t red_ldy;
   const float* red_bias;
-  // Quantization fused in front (a launch of the FQ form): the grid is 1-D;
-  // its first fq_prod work-groups each quantize one token row of the f32
-  // fq_x (row stride fq_ldx) into the Q8_K records at xq and the row's
-  // largest |d| into dmax (both written, so not const there), then count the
-  // row in fq_ready[row / token tile].  The other work-groups are the GEMM's
-  // fq_gx x fq_gy x (token tiles) grid, each waiting until its token tile's
-  // rows are in; the last of a tile's GEMM work-groups past the wait (counted
-  // in fq_done) sets both counters back to 0.  A wait that gives up sets
-  // *fq_err and goes on.
-  const float* fq_x;
-  int64_t fq_ldx;
-  int fq_prod, fq_gx, fq_gy;
-  uint32_t* fq_ready;
-  uint32_t* fq_done;
-  uint32_t* fq_err;
 };
 
 // Streaming LM head: at most 32 gathered Q8_K rows (xq, [M][SB] records)
@@ -82,10 +67,6 @@ hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 gr
 // The same kernels in their test form: the exact int32 super-block sums
 // A[m][n][sb] go to p.out instead of y; token tile qgemm_cfg_max_tb(cfg).
 hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s);
-// The FQ form (quantization fused in front; see GemmParams): token tile
-// qgemm_cfg_max_tb(cfg), a 1-D grid of p.fq_prod + fq_gx * fq_gy * token
-// tiles work-groups.
-hipError_t launch_qgemm_fq(int qtype, const GemmParams& p, int cfg, unsigned n_wgs, hipStream_t s);
 bool lmhead_stream_fits(int64_t K, int64_t n_rows);
 int lmhead_stream_waves();             // the most waves (key slots per row) it uses
 int64_t lmhead_stream_slots(int64_t N);  // the waves it uses for N rows

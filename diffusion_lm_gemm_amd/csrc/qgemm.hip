@@ -35,7 +35,6 @@
 // finish sums the slices in split order (no second kernel).
 #include "common.hpp"
 #include "kernels.hpp"
-#include "q8k.hpp"
 #include "unpack.hpp"
 
 namespace dllm {
@@ -125,70 +124,10 @@ __device__ __forceinline__ void sum_split_tile(const GemmParams& p, int64_t row_
 // reads zeros and makes no memory access.
 constexpr uint32_t kNoLoad = 0x80000000u;
 
-// FQ producer work-group: quantizes token row m of p.fq_x into its Q8_K
-// records at p.xq (the rule of q8k_block, so the same bytes as the quantizer
-// kernel writes) and its largest |d| into p.dmax, all with device-coherent
-// stores; once they are done, counts the row in for its token tile.  Each
-// wave takes the row's blocks wv, wv + NWV, ..., four at a time with their
-// loads in flight together (a block index past the row loads the row's last
-// block again and stores nothing).
-template <int NTH, int TOK>
-__device__ __forceinline__ void fq_produce(const GemmParams& p, int64_t m, int tid) {
-  constexpr int NWV = NTH / 64;
-  constexpr int QB = 4;
-  __shared__ float s_pmax[NWV];
-  const int lane = tid & 63, wv = tid >> 6;
-  const int64_t SB = p.SB;
-  const float* xrow = p.fq_x + m * p.fq_ldx;
-  const bool vec = ((((uintptr_t)xrow) & 15) == 0);
-  const rsrc_t yr = make_rsrc(p.xq, p.M * SB * Q8K_BYTES);
-  float wmax = 0.0f;
-  for (int64_t sb0 = wv; sb0 < SB; sb0 += NWV * QB) {
-    float v[QB][4];
-#pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const int64_t sb = sb0 + NWV * u < SB ? sb0 + NWV * u : SB - 1;
-      load4_f32(xrow + sb * QK + 4 * lane, vec, v[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const int64_t sb = sb0 + NWV * u;
-      const Q8Block b = q8k_block(v[u], lane);
-      if (sb < SB) {
-        const uint32_t off = (uint32_t)((m * SB + sb) * Q8K_BYTES);
-        buf_st32_dev(yr, off + 4 + 4 * lane, b.packed);
-        if ((lane & 3) == 0) buf_st16_dev(yr, off + 260 + 2 * (lane >> 2), (uint16_t)b.bsum);
-        if (lane == 0) buf_st32_dev(yr, off, __builtin_bit_cast(uint32_t, b.d));
-        wmax = fmaxf(wmax, __builtin_fabsf(b.d));
-      }
-    }
-  }
-  if (lane == 0) s_pmax[wv] = wmax;
-  __syncthreads();
-  if (tid == 0) {
-    float mx = s_pmax[0];
-#pragma unroll
-    for (int k = 1; k < NWV; ++k) mx = fmaxf(mx, s_pmax[k]);
-    buf_st32_dev(make_rsrc(p.dmax, p.M * 4), (uint32_t)(m * 4), __builtin_bit_cast(uint32_t, mx));
-  }
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) __hip_atomic_fetch_add(p.fq_ready + m / TOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// How long a GEMM work-group of the FQ form waits for its token tile's rows
-// before it gives up (about 0.1 s of s_sleep 4), sets *p.fq_err and goes on:
-// every wait ends.
-constexpr int kFqSpinLimit = 1 << 20;
-
 // SUMS: the test form of the same kernel, which also stores every tile's
 // exact int32 super-block sums A_sb = (hi << shift) + lo, as formed for the
 // epilogue, to ((int32_t*)p.out)[(m * N + n) * SB + sb], and writes no y.
-// FQ: the quantization of the activations fused in front, in producer
-// work-groups of the same launch (see GemmParams).  The producers come first
-// in the 1-D grid, so each is dispatched before every GEMM work-group of its
-// XCD and never waits on them.
-template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false, bool FQ = false>
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
   static_assert(NW == 4 || NW == 8 || NW == 12, "waves per work-group: 4, 8 or 12 (whole SIMDs)");
   constexpr bool ONE = (ST == 1);
@@ -240,28 +179,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int64_t N = p.N, SB = p.SB, M = p.M;
-  // grid position: row tile bx, K split by, token tile bz of gx x gy x ..
-  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z, gx = gridDim.x, gy = gridDim.y;
-  if constexpr (FQ) {
-    const int id = blockIdx.x;
-    if (id < p.fq_prod) {
-      fq_produce<NTH, TOK>(p, id, tid);
-      return;
-    }
-    const int g = id - p.fq_prod;
-    gx = p.fq_gx;
-    gy = p.fq_gy;
-    bx = g % gx;
-    by = (g / gx) % gy;
-    bz = g / (gx * gy);
-  }
-  // FQ: the activation records and dmax were written in this launch by
-  // work-groups on other XCDs, so they are read device-coherently
-  constexpr int XAUX = FQ ? kCoherentAux : 0;
-  const int64_t m0 = (int64_t)bz * TOK;
-  const int64_t s0 = (int64_t)by * p.sps;
+  const int64_t m0 = (int64_t)blockIdx.z * TOK;
+  const int64_t s0 = (int64_t)blockIdx.y * p.sps;
   const int64_t s1 = (s0 + p.sps < SB) ? s0 + p.sps : SB;
-  const int64_t row0 = (int64_t)bx * ROWS + wv * 16 * RB;  // first row of this wave
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS + wv * 16 * RB;  // first row of this wave
   // Buffer resources: loads past num_records read as zero (rows >= N,
   // tokens >= M).  The host keeps both operands below 2 GiB.
   const rsrc_t wr = make_rsrc(p.w, N * SB * BYTES);
@@ -309,7 +230,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       const int tok = (wv * DPW + k) * 4 + (lane >> 4);
       const uint32_t voff = dma_tok0 + k * tok_step + 16 * ((lane & 15) ^ (tok & 15));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(stage + (wv * DPW + k) * 1024), 16, voff, soff, 0, XAUX);
+          xr, (__attribute__((address_space(3))) void*)(stage + (wv * DPW + k) * 1024), 16, voff, soff, 0, 0);
     }
   };
   // idx_b: Q4_K bsum pairs (2j, 2j+1) for j = 4q .. 4q+3, one per dword
@@ -325,8 +246,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       const int it_c = item < NITEM ? item : NITEM - 1;
       const int tok = MINS ? (it_c >> 1) : it_c;
       const uint32_t xoff = (uint32_t)(((m0 + tok) * SB + sb) * Q8K_BYTES);
-      idx_d[k] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)xoff, 0, XAUX);
-      if constexpr (MINS) idx_b[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xoff + 260 + 16 * (it_c & 1)), 0, XAUX);
+      idx_d[k] = buf_ld32(xr, xoff);
+      if constexpr (MINS) idx_b[k] = buf_ld128(xr, xoff + 260 + 16 * (it_c & 1));
     }
   };
   auto items_store = [&](int buf, int slot8) {
@@ -653,28 +574,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // first, so that their latency overlaps the pre-scale scan below.
 #pragma unroll
   for (int b = 0; b < RB; ++b) load_raw<QT>(wr, wrow_off[b] + (uint32_t)(s0 * BYTES), g4, raw[b]);
-  if constexpr (FQ) {
-    // wait (bounded) for the token tile's rows; the weights are on their way
-    if (tid == 0) {
-      const uint32_t need = (uint32_t)(M - m0 < TOK ? M - m0 : TOK);
-      uint32_t* rdy = p.fq_ready + bz;
-      int spins = 0;
-      while (__hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-        if (++spins > kFqSpinLimit) {
-          __hip_atomic_store(p.fq_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-      }
-      // the last of the tile's GEMM work-groups past the wait resets the counters
-      const uint32_t before = __hip_atomic_fetch_add(p.fq_done + bz, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (before + 1 == (uint32_t)(gx * gy)) {
-        __hip_atomic_store(rdy, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.fq_done + bz, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  }
   if constexpr (!ONE) {
     act_dma(s_act0, s0);
     items_load(s0);
@@ -690,18 +589,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     if constexpr (MINS) {
       float mx = 0.0f;
       if (p.dmax) {
-        if (m0 + tid < M)
-          mx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.dmax, M * 4),
-                                                                              (int)((m0 + tid) * 4), 0, XAUX));
+        if (m0 + tid < M) mx = p.dmax[m0 + tid];
       } else {
         // sixteen independent loads in flight per round
         const uint32_t tok_off = (uint32_t)((m0 + tid) * SB * Q8K_BYTES);
         for (int64_t sb = 0; sb < SB; sb += 16) {
           float v[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            v[u] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(tok_off + (uint32_t)((sb + u) * Q8K_BYTES)), 0, XAUX));
+          for (int u = 0; u < 16; ++u) v[u] = __builtin_bit_cast(float, buf_ld32(xr, tok_off + (uint32_t)((sb + u) * Q8K_BYTES)));
 #pragma unroll
           for (int u = 0; u < 16; ++u) mx = (sb + u < SB) ? fmaxf(mx, __builtin_fabsf(v[u])) : mx;
         }
@@ -756,11 +651,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // (plus the bias of those rows, when given: only without a K split, whose
   // reduction adds it instead)
   if constexpr (SUMS) return;
-  float* outp = p.out + (int64_t)by * p.split_stride;
+  float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
   // K split with the reduction fused: the slice [M][ldo] goes out with
   // device-coherent 16-byte stores (ldo a multiple of 64 >= N, so every
   // group of four rows that starts inside N is whole)
-  const rsrc_t wsr = make_rsrc(p.out, p.tile_cnt ? (int64_t)gy * p.split_stride * 4 : 0);
+  const rsrc_t wsr = make_rsrc(p.out, p.tile_cnt ? (int64_t)gridDim.y * p.split_stride * 4 : 0);
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int64_t nbase = row0 + 16 * b + 4 * g4;
@@ -778,7 +673,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       yacc[b][t] = yv;
       if (p.tile_cnt) {
         if (m < M && nbase < N)
-          buf_st128_dev(wsr, (uint32_t)(((int64_t)by * p.split_stride + m * p.ldo + nbase) * 4),
+          buf_st128_dev(wsr, (uint32_t)(((int64_t)blockIdx.y * p.split_stride + m * p.ldo + nbase) * 4),
                         __builtin_bit_cast(v4u, yv));
       } else if (m < M) {
         float* dst = outp + m * p.ldo + nbase;
@@ -808,14 +703,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     wait_vmem();
     __syncthreads();
     if (tid == 0) {
-      uint32_t* c = p.tile_cnt + (int64_t)bz * gx + bx;
+      uint32_t* c = p.tile_cnt + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
       const uint32_t before = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = (before + 1 == (uint32_t)gy);
+      const bool last = (before + 1 == gridDim.y);
       if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last ? 1 : 0;
     }
     __syncthreads();
-    if (s_last) sum_split_tile<ROWS, TOK, NTH>(p, (int64_t)bx * ROWS, m0, gy, tid);
+    if (s_last) sum_split_tile<ROWS, TOK, NTH>(p, (int64_t)blockIdx.x * ROWS, m0, (int)gridDim.y, tid);
   }
 
   if constexpr (ARGMAX) {
@@ -859,12 +754,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       uint64_t best = s_key[tid];
 #pragma unroll
       for (int k = 1; k < NW; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
-      if (m < M) p.keys[(int64_t)bx * M + m] = best;
+      if (m < M) p.keys[(int64_t)blockIdx.x * M + m] = best;
       if (p.stats) {
         float sm = s_stat[tid].x, ss = s_stat[tid].y;
 #pragma unroll
         for (int k = 1; k < NW; ++k) softmax_merge(sm, ss, s_stat[k * TOK + tid].x, s_stat[k * TOK + tid].y);
-        if (m < M) p.stats[(int64_t)bx * M + m] = float2{sm, ss};
+        if (m < M) p.stats[(int64_t)blockIdx.x * M + m] = float2{sm, ss};
       }
     }
   }
@@ -948,9 +843,9 @@ __global__ __launch_bounds__(256) void k_partials(const uint8_t* __restrict__ w,
 }
 
 // ---- host-side launch helpers -------------------------------------------
-template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false, bool FQ = false>
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
 static hipError_t launch_k(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX, ST, SUMS, FQ>), grid, dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((k_qgemm<QT, TB, NW, RB, ARGMAX, ST, SUMS>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1020,25 +915,6 @@ static hipError_t launch_sums_cfg(const GemmParams& p, int cfg, dim3 grid, hipSt
     case 6: return launch_k<QT, 5, 4, 1, false, 2, true>(p, grid, s);
     default: return launch_k<QT, 5, 12, 1, false, 2, true>(p, grid, s);
   }
-}
-
-// The FQ form of each tile configuration, at its largest token tile.
-template <int QT>
-static hipError_t launch_fq_cfg(const GemmParams& p, int cfg, dim3 grid, hipStream_t s) {
-  switch (cfg) {
-    case 1: return launch_k<QT, 10, 4, 1, false, 2, false, true>(p, grid, s);
-    case 2: return launch_k<QT, 10, 8, 1, false, 2, false, true>(p, grid, s);
-    case 3: return launch_k<QT, 5, 8, 2, false, 2, false, true>(p, grid, s);
-    case 4: return launch_k<QT, 5, 4, 2, false, 2, false, true>(p, grid, s);
-    case 5: return launch_k<QT, 10, 4, 1, false, 1, false, true>(p, grid, s);
-    case 6: return launch_k<QT, 5, 4, 1, false, 2, false, true>(p, grid, s);
-    default: return launch_k<QT, 5, 12, 1, false, 2, false, true>(p, grid, s);
-  }
-}
-
-hipError_t launch_qgemm_fq(int qtype, const GemmParams& p, int cfg, unsigned n_wgs, hipStream_t s) {
-  if (qtype == QT_Q4K) return launch_fq_cfg<QT_Q4K>(p, cfg, dim3(n_wgs), s);
-  return launch_fq_cfg<QT_Q6K>(p, cfg, dim3(n_wgs), s);
 }
 
 hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s) {

@@ -16,7 +16,6 @@
 // scale from it instead of scanning every block's d.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "q8k.hpp"
 
 namespace dllm {
 
@@ -24,18 +23,76 @@ namespace {
 
 constexpr int QW = 16;  // waves per work-group (one token row)
 
+// DPP controls (quad permutes and row mirrors move data inside 4- and
+// 16-lane groups without touching LDS).
+constexpr int DPP_QUAD_SWAP1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int DPP_QUAD_SWAP2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15 - i within a row of 16
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within a half row
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Largest of a non-negative f32 (as its bits, which order like the values)
+// over the wave; the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t v) {
+  v = max(v, dpp<DPP_QUAD_SWAP1>(v));
+  v = max(v, dpp<DPP_QUAD_SWAP2>(v));
+  v = max(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dpp<DPP_ROW_MIRROR>(v));  // every lane holds its row's maximum
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // Quantize one 256-value block held as v[0..3] = values 4 lane .. 4 lane + 3
 // into the 292-byte record at `out` (written only if `store`; its d only if
 // also `store_d`); returns d (0 if not `store`).
 __device__ __forceinline__ float quantize_block(const float (&v)[4], uint8_t* out, int lane, bool store,
                                                bool store_d = true) {
-  const Q8Block b = q8k_block(v, lane);
-  if (store) {
-    ((uint32_t*)(out + 4))[lane] = b.packed;
-    if ((lane & 3) == 0) ((int16_t*)(out + 260))[lane >> 2] = (int16_t)(int32_t)b.bsum;
-    if (lane == 0 && store_d) *(float*)out = b.d;
+#pragma clang fp contract(off)
+  float a[4];
+  float lm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_fabsf(v[i]);
+    lm = fmaxf(lm, a[i]);
   }
-  return store ? b.d : 0.0f;
+  const float amax = __builtin_bit_cast(float, wave_max_bits(__builtin_bit_cast(uint32_t, lm)));
+  // an all-zero block gives d = 0 and zero quants (selects, not a branch)
+  const bool zero = (amax == 0.0f);
+  // the pivot: the first value of largest magnitude, i.e. the lowest lane
+  // holding the maximum and, inside it, the lowest position
+  const int first = (a[0] == amax) ? 0 : (a[1] == amax) ? 1 : (a[2] == amax) ? 2 : (a[3] == amax) ? 3 : 4;
+  const uint64_t holders = __ballot(first < 4);
+  const int src_lane = __builtin_ctzll(holders);
+  const float pv = (first == 0) ? v[0] : (first == 1) ? v[1] : (first == 2) ? v[2] : v[3];
+  const float pivot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), src_lane));
+  const float iscale = -127.0f / (zero ? 1.0f : pivot);
+  int q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = iscale * v[i];
+    const int t = (int)__builtin_rintf(p);
+    q[i] = zero ? 0 : (t > 127 ? 127 : t);
+  }
+  const uint32_t packed = (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) |
+                          ((uint32_t)(q[2] & 255) << 16) | ((uint32_t)(q[3] & 255) << 24);
+  // sum of 16 = the four lanes of a quad
+  uint32_t s = (uint32_t)(q[0] + q[1] + q[2] + q[3]);
+  s += dpp<DPP_QUAD_SWAP1>(s);
+  s += dpp<DPP_QUAD_SWAP2>(s);
+  const float d = zero ? 0.0f : 1.0f / iscale;
+  if (store) {
+    ((uint32_t*)(out + 4))[lane] = packed;
+    if ((lane & 3) == 0) ((int16_t*)(out + 260))[lane >> 2] = (int16_t)(int32_t)s;
+    if (lane == 0 && store_d) *(float*)out = d;
+  }
+  return store ? d : 0.0f;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 11
+#define DLLM_ABI_VERSION 10
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -186,48 +186,6 @@ int dllm_qgemm_bias(int qtype, const void *w, int64_t N, int64_t K,
                     const void *x_q8k, const float *x_dmax, int64_t M,
                     const float *bias, float *y, int64_t ldy, void *workspace,
                     int64_t workspace_bytes, void *stream);
-
-/*
- * Quantize and multiply in one launch: x (f32 [M][ldx], ldx >= K, 4-byte
- * aligned) is quantized per token to Q8_K exactly as dllm_quantize_q8k does
- * (the records go to x_q8k, [M][K/256] x 292 bytes, and each token's largest
- * |d| to x_dmax, f32 [M]; both written, so a second GEMM on the same input
- * can reuse them), then y = W_hat X_hat^T (+ bias) as dllm_qgemm_bias
- * computes it, bit for bit (Development plan, "Compute design": a step is a
- * stream of quantize + GEMM).  The first M work-groups of the launch
- * quantize one token row each; the GEMM's work-groups wait (on a counter per
- * token tile, with device-coherent loads) only for their own tokens' rows, so
- * the quantization overlaps the first weight loads.  The producer work-groups
- * come first in the grid and never wait, so they are dispatched before every
- * GEMM work-group of their XCD.  A wait gives up after about 0.1 s and sets
- * the u32 at byte 57344 of the workspace to 1 (the result is then wrong;
- * the word stays set until the caller clears it).
- *   workspace  at least dllm_quantize_qgemm_workspace_bytes(qtype, N, K, M)
- *              bytes (>= 65536), 16-byte aligned, zero-filled once before
- *              first use; its first 64 KiB hold the counters, which every
- *              call leaves at zero; calls sharing one are ordered on one
- *              stream.  With a workspace too small for the planned K split
- *              the call runs unsplit.
- * M may make at most 1024 token tiles (DLLM_E_SHAPE otherwise).
- */
-int64_t dllm_quantize_qgemm_workspace_bytes(int qtype, int64_t N, int64_t K,
-                                            int64_t M);
-int dllm_quantize_qgemm(int qtype, const void *w, int64_t N, int64_t K,
-                        const float *x, int64_t ldx, int64_t M,
-                        const float *bias, void *x_q8k, float *x_dmax,
-                        float *y, int64_t ldy, void *workspace,
-                        int64_t workspace_bytes, void *stream);
-/*
- * Test-only: dllm_quantize_qgemm with the tile configuration (1..7) and K
- * split (1..K/256) given, as dllm_qgemm_planned; a split needs its workspace
- * (DLLM_E_WORKSPACE otherwise).
- */
-int dllm_quantize_qgemm_planned(int qtype, const void *w, int64_t N, int64_t K,
-                                const float *x, int64_t ldx, int64_t M,
-                                const float *bias, void *x_q8k, float *x_dmax,
-                                float *y, int64_t ldy, void *workspace,
-                                int64_t workspace_bytes, int tile, int split,
-                                void *stream);
 
 /*
  * dllm_qgemm_bias for callers that cannot allocate device memory (code under

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 21
+    assert len(names) == 18
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -232,21 +232,3 @@ def test_no_environment_reads_in_the_library():
     for name in os.listdir(csrc):
         if name.endswith((".hip", ".hpp", ".h", ".cpp")):
             assert "getenv" not in open(os.path.join(csrc, name)).read(), name
-
-
-def test_quantize_qgemm_argument_errors(dl):
-    """The quantize-and-multiply entry validates on the host: pointers, ldx,
-    the 64 KiB minimum workspace and its alignment, the planned form's tile."""
-    L = dl.lib
-    ws = ctypes.c_void_p(1 << 24)
-    big = 1 << 30
-    args = lambda x=FAKE, ldx=1024, wsp=ws, wsb=big: (dl.Q4_K, FAKE, 64, 1024, x, ldx, 8, None, FAKE, FAKE, FAKE, 64,
-                                                      wsp, wsb)
-    assert L.dllm_quantize_qgemm(*args(x=None), None) == dl.E_ARG
-    assert L.dllm_quantize_qgemm(*args(ldx=512), None) == dl.E_ARG
-    assert L.dllm_quantize_qgemm(*args(wsb=65535), None) == dl.E_WORKSPACE
-    assert L.dllm_quantize_qgemm(*args(wsp=ctypes.c_void_p((1 << 24) + 8)), None) == dl.E_ALIGN
-    assert L.dllm_quantize_qgemm_planned(*args(), 0, 1, None) == dl.E_ARG
-    assert L.dllm_quantize_qgemm_planned(*args(), 9, 1, None) == dl.E_ARG
-    assert L.dllm_quantize_qgemm_planned(*args(), 1, 5, None) == dl.E_ARG
-    assert dl.lib.dllm_quantize_qgemm_workspace_bytes(dl.Q4_K, 64, 1024, 8) >= 65536

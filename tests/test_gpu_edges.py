@@ -13,6 +13,8 @@ exact integer sums.
   configuration forms on the matrix cores, bit-exact against the oracle's
   per-16 partial dots combined with the blocks' integer scales (mojo-dllm
   Development plan, "Compute design": the per-16 integer scale form).
+* A token's output does not depend on how many tokens share its work-group
+  (the token tile): bit-identical between a small and the largest tile.
 Bars as in test_gpu_parity: f32 outputs within 1e-4 * (|oracle| + rms(row))
 and below 5% of that bound; integers bit-exact.
 """
@@ -170,3 +172,26 @@ def test_lmhead_edges_both_paths(dl, path, case):
     _check_argmax(lg, am.cpu().numpy(), ref, ref_am, f"lmhead {case} path={path}")
     _check_confidence(lg, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
                       f"lmhead {case} path={path}")
+
+
+# --------------------------------------------- token tile independence ----
+@pytest.mark.parametrize("q,tile", [(12, 5), (12, 1), (12, 6), (14, 5), (14, 2)])
+def test_token_tile_does_not_change_y(dl, q, tile):
+    """37 tokens (a token tile of 3 x 16) give bit for bit the same y as the
+    same 37 rows of a 160-token call (the configuration's largest tile):
+    every instantiation forms and splits the same f32 values (Q4_K's min
+    term in f16 halves, the per-super-block fma), unsplit and with a K
+    split; activations over six decades of scale."""
+    N, K, M = 333, 3072, 37
+    _say(f"token tile independence q={q} tile={tile}")
+    w = synth.qk_rows(q, N, K, 74, f"tt-{q}").to(DEV)
+    x = synth.normal_f32((M, K), 74, "tt-x").to(DEV) * torch.logspace(-3, 3, M, device=DEV).unsqueeze(1)
+    xp = torch.zeros((160, K), device=DEV)
+    xp[:M] = x
+    dm, dmp = torch.empty(M, device=DEV), torch.empty(160, device=DEV)
+    xq, xqp = dl.quantize_q8k(x, dmax=dm), dl.quantize_q8k(xp, dmax=dmp)
+    for split in (1, 3):
+        a = dl.qgemm_planned(q, w, N, K, xq, M, tile=tile, split=split, x_dmax=dm)
+        b = dl.qgemm_planned(q, w, N, K, xqp, 160, tile=tile, split=split, x_dmax=dmp)[:M]
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"split {split}"
