@@ -520,7 +520,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       // the next block's chunks, spread over the tiles
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if ((c * TB) / 4 == t) unpack_chunk<QT>(raw[0], g4, c, sc03, sc47, An.lo[c], An.hi[c]);
+        if ((c * TB) / 4 == t) {
+          unpack_chunk<QT>(raw[0], g4, c, sc03, sc47, An.lo[c], An.hi[c]);
+          // pinned here (with four waves, which have the registers):
+          // otherwise the compiler sinks the unpack to the next step, where
+          // it runs as one burst ahead of that step's first MFMA
+          if constexpr (NW == 4) asm volatile("" : "+v"(An.lo[c]), "+v"(An.hi[c]));
+        }
       if (t == (3 * TB) / 4) load_raw<QT>(wr, noff, g4, raw[0]);
       if (t == TB - 1) {
 #pragma unroll
