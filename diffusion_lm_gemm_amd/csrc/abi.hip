@@ -151,7 +151,7 @@ struct Tuned {
 constexpr Tuned kTuned[] = {
     {12, 24576, 4096, 129, 160, 7, 1},  // gate + up
     {12, 12288, 4096, 129, 160, 7, 2},  // Q + K + V
-    {12, 8192, 4096, 129, 160, 6, 2},   // Q + K (V in Q6_K)
+    {12, 8192, 4096, 129, 160, 6, 1},   // Q + K (V in Q6_K)
     {12, 4096, 4096, 129, 160, 6, 4},   // O
     {14, 4096, 4096, 129, 160, 5, 4},   // V
     {12, 4096, 12288, 129, 160, 6, 4},  // down
