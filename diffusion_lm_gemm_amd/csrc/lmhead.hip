@@ -13,6 +13,8 @@
 // planes on v_mfma_i32_16x16x64_i8, the per-super-block f32 epilogue, and for
 // Q4_K the min term on f16 MFMA), and each wave keeps, per token, the largest
 // (logit, lowest row) key over its rows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "unpack.hpp"
@@ -24,7 +26,15 @@ constexpr int LM_SBMAX = 16;  // K <= 4096
 
 // Keys are (order-preserving f32 bits << 32) | ~row: the largest key is the
 // largest logit, and among equal logits the lowest row.
-template <int QT, int NW>
+//
+// PARITY (Q6_K with an even number of super-blocks per row): a 210-byte
+// block then starts 4-byte aligned exactly when its super-block index is
+// even, the same for every lane of a step, and step st of a wave's stream has
+// the parity of st.  Even blocks are loaded without the alignment dwords and
+// used without byte shifts; the loop runs six steps per iteration so that
+// each step's parity and buffer are fixed at compile time.  The stream is
+// bound by its vector-memory instructions, of which this removes a quarter.
+template <int QT, int NW, bool PARITY>
 __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
@@ -125,9 +135,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
     if (++s == SB) { s = 0; ++kk; }
   };
 
-  auto step = [&](uint32_t(&rw)[RAWW]) {
+  // PAR: 0 = alignment from the offset (any SB), 1 = this block 4-byte
+  // aligned and the one three steps ahead not (SB even, sb even), 2 = the
+  // other way round
+  auto step = [&](auto par_tag, uint32_t(&rw)[RAWW]) {
+    constexpr int PAR = decltype(par_tag)::value;
     uint32_t raw[RAW];
-    align_raw<QT>(rw, woff(k, sb), raw);
+    if constexpr (PAR == 1 && QT == QT_Q6K) {
+#pragma unroll
+      for (int f = 0; f < 5; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[4 * f + i] = rw[5 * f + i];
+      raw[20] = rw[25];
+    } else {
+      align_raw<QT>(rw, woff(k, sb), raw);
+    }
     v4i alo[4], ahi[4];
     const float drow = unpack<QT>(raw, g4, alo, ahi);
     if constexpr (MINS) {
@@ -137,7 +159,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
       mh3 = mine ? raw[3] : mh3;
     }
     // the block three steps ahead (past the end: reads nothing that is used)
-    load_raw_dw<QT>(wr, woff(k2, sb2), g4, rw);
+    if constexpr (PAR == 2 && QT == QT_Q6K) {
+      // 4-byte aligned: the five 16-byte fields and d, no alignment dwords
+      const uint32_t off = woff(k2, sb2);
+      const uint32_t fo[5] = {off + 16 * g4, off + 64 + 16 * g4, off + 128 + 16 * (g4 & 1), off + 160 + 16 * (g4 & 1),
+                              off + 192};
+#pragma unroll
+      for (int f = 0; f < 5; ++f) {
+        const v4u v = buf_ld128(wr, fo[f]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rw[5 * f + i] = v[i];
+      }
+      rw[25] = buf_ld16(wr, off + 208);
+    } else {
+      load_raw_dw<QT>(wr, woff(k2, sb2), g4, rw);
+    }
     advance(k2, sb2);
     float dsel[4];
 #pragma unroll
@@ -230,14 +266,35 @@ __global__ __launch_bounds__(64 * NW, 1) void k_lmhead_stream(LmParams p) {
   advance(k2, sb2);
   load_raw_dw<QT>(wr, woff(k2, sb2), g4, rawC);
   advance(k2, sb2);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
   int64_t st = 0;
-  for (; st + 2 < n_steps; st += 3) {
-    step(rawA);
-    step(rawB);
-    step(rawC);
+  if constexpr (PARITY) {
+    // step st has sb of the parity of st; six steps per iteration cover both
+    // parities on all three buffers
+    for (; st + 5 < n_steps; st += 6) {
+      step(P1{}, rawA);
+      step(P2{}, rawB);
+      step(P1{}, rawC);
+      step(P2{}, rawA);
+      step(P1{}, rawB);
+      step(P2{}, rawC);
+    }
+    if (st < n_steps) step(P1{}, rawA);
+    if (st + 1 < n_steps) step(P2{}, rawB);
+    if (st + 2 < n_steps) step(P1{}, rawC);
+    if (st + 3 < n_steps) step(P2{}, rawA);
+    if (st + 4 < n_steps) step(P1{}, rawB);
+  } else {
+    for (; st + 2 < n_steps; st += 3) {
+      step(P0{}, rawA);
+      step(P0{}, rawB);
+      step(P0{}, rawC);
+    }
+    if (st < n_steps) step(P0{}, rawA);
+    if (st + 1 < n_steps) step(P0{}, rawB);
   }
-  if (st < n_steps) step(rawA);
-  if (st + 1 < n_steps) step(rawB);
 
   // per token: best key over the wave's rows (lanes of one token differ in g4)
 #pragma unroll
@@ -272,9 +329,11 @@ hipError_t launch_lmhead_stream(int qtype, const LmParams& p, hipStream_t s) {
   const int64_t wgs_needed = (n_rb + LM_NW - 1) / LM_NW;
   const unsigned grid = (unsigned)(wgs_needed < 256 ? wgs_needed : 256);
   if (qtype == QT_Q4K)
-    hipLaunchKernelGGL((k_lmhead_stream<QT_Q4K, LM_NW>), dim3(grid), dim3(64 * LM_NW), 0, s, p);
+    hipLaunchKernelGGL((k_lmhead_stream<QT_Q4K, LM_NW, false>), dim3(grid), dim3(64 * LM_NW), 0, s, p);
+  else if (p.SB % 2 == 0)
+    hipLaunchKernelGGL((k_lmhead_stream<QT_Q6K, LM_NW, true>), dim3(grid), dim3(64 * LM_NW), 0, s, p);
   else
-    hipLaunchKernelGGL((k_lmhead_stream<QT_Q6K, LM_NW>), dim3(grid), dim3(64 * LM_NW), 0, s, p);
+    hipLaunchKernelGGL((k_lmhead_stream<QT_Q6K, LM_NW, false>), dim3(grid), dim3(64 * LM_NW), 0, s, p);
   return hipGetLastError();
 }
 
