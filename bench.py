@@ -926,7 +926,8 @@ def summarize_traffic(target, prefix, out):
 def _kernel_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "kernels.hpp", "unpack.hpp", "qgemm.hip", "quantize.hip", "abi.hip"):
+    for f in ("common.hpp", "kernels.hpp", "unpack.hpp", "qgemm.hip", "quantize.hip", "abi.hip", "lmhead.hip",
+              "attention.hip"):
         h.update(open(os.path.join(ROOT, "diffusion_lm_gemm_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
