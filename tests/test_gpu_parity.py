@@ -642,3 +642,23 @@ def test_lmhead_full_size(dl, M, first):
     assert np.array_equal(lg2.cpu().numpy(), logits) and np.array_equal(am2.cpu().numpy(), am)
     _check_confidence(logits, lse.cpu().numpy().astype(np.float64), p.cpu().numpy().astype(np.float64), ref,
                       "lmhead full confidence")
+
+
+@pytest.mark.parametrize("K", [1024, 1280, 1536])
+def test_lmhead_stream_phases(dl, K):
+    """The streaming LM head with three 16-row blocks per wave (98304 rows
+    over 2048 waves), so that its loop (six steps per iteration in the form
+    for an even number of super-blocks per row, three in the other) crosses
+    row-block boundaries at every phase: K = 1024 and 1536 (4 and 6
+    super-blocks, the even form), K = 1280 (5, the general form); whole
+    oracle rows, argmax and ties as everywhere."""
+    N, M = 98304, 148
+    _say(f"lmhead stream phases K={K}")
+    w = _weights(14, N, K, 15, f"lm-phase-{K}")
+    h = synth.normal_f32((M, K), 15, f"lm-phase-h-{K}")
+    rows = synth.distinct_rows(32, M, 15, f"lm-phase-rows-{K}")
+    ref, ref_am = oracle.lmhead(14, w.numpy(), N, K, h.numpy(), rows.numpy())
+    logits, am = dl.lmhead_masked(14, w.to(DEV), N, K, h.to(DEV), rows.to(DEV))
+    logits = logits.cpu().numpy(); am = am.cpu().numpy()
+    assert_close_rows(logits, ref, f"lmhead stream phases K={K}")
+    _check_argmax(logits, am, ref, ref_am, f"lmhead stream phases K={K}")
