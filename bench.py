@@ -150,8 +150,9 @@ def dream_step(dl, synth, torch, dev, L, seed, graph_node_ms):
     amax = torch.empty(masked, dtype=torch.int32, device=dev)
     shapes = [(Q4, NQKV - HKV * HD, D), (Q6, HKV * HD, D), (Q4, NQKV, D), (Q4, D, D), (Q4, 2 * FFN, D),
               (Q4, D, FFN), (Q6, D, FFN)]
-    ws = torch.zeros(max(256, max(dl.qgemm_workspace_bytes(q, n, k, L) for q, n, k in shapes)),
-                     dtype=torch.uint8, device=dev)
+    nqk = NQKV - HKV * HD
+    ws = torch.zeros(max(256, max(dl.qgemm_workspace_bytes(q, n, k, L) for q, n, k in shapes),
+                         dl.qgemm_pair_workspace_bytes(Q4, nqk, Q6, HKV * HD, D, L)), dtype=torch.uint8, device=dev)
     ws_lm = torch.empty(dl.lmhead_workspace_bytes(Q6, VOC, D, masked), dtype=torch.uint8, device=dev)
     fns, byts, ops = [], 0, 0
 
@@ -168,10 +169,13 @@ def dream_step(dl, synth, torch, dev, L, seed, graph_node_ms):
 
     for lw in lay:
         quant(x_d, xq_d, dm_d)
-        if lw["even"]:
-            nqk = NQKV - HKV * HD
-            gemm(Q4, lw["qk"], nqk, D, xq_d, dm_d, y_qkv[:, :nqk], lw["bias"][:nqk])
-            gemm(Q6, lw["v"], HKV * HD, D, xq_d, dm_d, y_qkv[:, nqk:], lw["bias"][nqk:])
+        if lw["even"]:  # Q + K (Q4_K) and V (Q6_K) in one launch
+            fns.append(lambda lw=lw: dl.qgemm_pair((Q4, lw["qk"], nqk, y_qkv[:, :nqk], lw["bias"][:nqk]),
+                                                   (Q6, lw["v"], HKV * HD, y_qkv[:, nqk:], lw["bias"][nqk:]), D,
+                                                   xq_d, L, workspace=ws, x_dmax=dm_d))
+            byts += (nqk * D // 256 * dl.block_bytes(Q4) + HKV * HD * D // 256 * dl.block_bytes(Q6)
+                     + L * D // 256 * 292 + L * NQKV * 4)
+            ops += 2 * L * NQKV * D
         else:
             gemm(Q4, lw["qkv"], NQKV, D, xq_d, dm_d, y_qkv, lw["bias"])
         quant(x_d, xq_d, dm_d)
@@ -411,9 +415,9 @@ def main():
         y_down = torch.empty((Lc, D), dtype=torch.float32, device=dev)
         logits = torch.empty((MASKED, VOCAB), dtype=torch.float32, device=dev)
         amax = torch.empty(MASKED, dtype=torch.int32, device=dev)
-        ws_bytes = max(dl.qgemm_workspace_bytes(q, n, k, Lc) for q, n, k in
-                       [(Q4, 3 * D, D), (Q4, 2 * D, D), (Q6, D, D), (Q4, D, D), (Q4, 2 * FFN, D),
-                        (Q4, D, FFN), (Q6, D, FFN)])
+        ws_bytes = max([dl.qgemm_workspace_bytes(q, n, k, Lc) for q, n, k in
+                        [(Q4, 3 * D, D), (Q4, D, D), (Q4, 2 * FFN, D), (Q4, D, FFN), (Q6, D, FFN)]]
+                       + [dl.qgemm_pair_workspace_bytes(Q4, 2 * D, Q6, D, D, Lc)])
         ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         ws_lm = torch.empty(dl.lmhead_workspace_bytes(Q6, VOCAB, D, MASKED), dtype=torch.uint8, device=dev)
         hidden = synth.normal_f32((Lc, D), seed, f"hidden-{Lc}", dev)
@@ -432,15 +436,21 @@ def main():
             calls.append((kind, lambda: dl.qgemm(q, w, N, K, xq, Lc, y=y, workspace=ws, x_dmax=dmax), byts,
                           2 * Lc * N * K, (kind, N, K)))
 
+        def add_pair(qa, wa, Na, ya, qb, wb, Nb, yb, K, xq, dmax):
+            """Two GEMMs of one input in one launch (dllm_qgemm_pair)."""
+            byts = (Na * K // 256 * bb(qa) + Nb * K // 256 * bb(qb) + Lc * K // 256 * 292 + Lc * (Na + Nb) * 4)
+            calls.append(("qgemm_pair", lambda: dl.qgemm_pair((qa, wa, Na, ya, None), (qb, wb, Nb, yb, None), K, xq,
+                                                              Lc, workspace=ws, x_dmax=dmax),
+                          byts, 2 * Lc * (Na + Nb) * K, ("qgemm_pair", f"{Na}+{Nb}", K)))
+
         for l, lw in enumerate(layers):
             x_norm = synth.normal_f32((Lc, D), seed, f"L{l:02d}.x_norm-{Lc}", dev)
             attn = synth.normal_f32((Lc, D), seed, f"L{l:02d}.attn-{Lc}", dev)
             h_norm = synth.normal_f32((Lc, D), seed, f"L{l:02d}.h_norm-{Lc}", dev)
             act = synth.normal_f32((Lc, FFN), seed, f"L{l:02d}.act-{Lc}", dev)
             add_quant(x_norm, xq_d, dmax_d)
-            if lw["even"]:
-                add_gemm(Q4, lw["qk"], 2 * D, D, xq_d, dmax_d, y_qkv[:, :2 * D])
-                add_gemm(Q6, lw["v"], D, D, xq_d, dmax_d, y_qkv[:, 2 * D:])
+            if lw["even"]:  # Q + K (Q4_K) and V (Q6_K) in one launch
+                add_pair(Q4, lw["qk"], 2 * D, y_qkv[:, :2 * D], Q6, lw["v"], D, y_qkv[:, 2 * D:], D, xq_d, dmax_d)
             else:
                 add_gemm(Q4, lw["qkv"], 3 * D, D, xq_d, dmax_d, y_qkv)
             add_quant(attn, xq_d, dmax_d)
@@ -570,12 +580,12 @@ def main():
                                               B["ws_lm"]))
     configs["4_lmhead_q6k"] = standalone(lm, [w_out], B["lm_bytes"], 2 * MASKED * VOCAB * D,
                                          f"config 4: masked LM head, {MASKED} of {L} rows x {VOCAB}x{D} Q6_K")
-    # config 3: one even layer's stream (4 quantizes, Q+K, V, O, gate+up, down
-    # in Q4_K / Q6_K as in the step), cycling the step's 16 even layers
+    # config 3: one even layer's stream (4 quantizes, Q+K with V, O, gate+up,
+    # down in Q4_K / Q6_K as in the step), cycling the step's 16 even layers
     layer_calls = []
     ci = 0
     for lw in layers:
-        n = 10 if lw["even"] else 9  # quantize, Q+K, V, quantize, O, quantize, gate/up, quantize, down
+        n = 8  # quantize, Q+K+V (one call: QKV, or the Q+K / V pair), quantize, O, quantize, gate/up, quantize, down
         if lw["even"]:
             layer_calls.append(calls[ci:ci + n])
         ci += n
@@ -595,7 +605,8 @@ def main():
         "int8_TOPS": round(l_ops / (ms3 * 1e-3) / 1e12, 2), "algorithmic_bytes": l_bytes, "int8_ops": l_ops,
         "calls_per_layer": len(layer_calls[0]), "layers_per_replay": R3,
         "weight_bytes_cycled": sum(c[2] for lc in layer_calls for c in lc),
-        "workload": f"config 3: one layer's stream at L={L} (4 quantizes; Q+K, O, gate+up Q4_K; V, down Q6_K)",
+        "workload": f"config 3: one layer's stream at L={L} (4 quantizes; Q+K, O, gate+up Q4_K; V, down Q6_K; "
+                    f"Q+K and V in one launch)",
         "timing": f"one graph of {R3} layer passes cycling the step's {len(layer_calls)} even layers, median of 5 replays"}
 
     # the dominant call (gate/up, a third of the step) stand-alone: the

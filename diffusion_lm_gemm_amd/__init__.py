@@ -33,6 +33,7 @@ HEADER_EXPORTS = (
     "dllm_qgemm_workspace_bytes", "dllm_qgemm", "dllm_qgemm_bias", "dllm_lmhead_workspace_bytes",
     "dllm_lmhead_masked", "dllm_lmhead_confidence", "dllm_qgemm_partials_i32",
     "dllm_qgemm_superblock_sums_i32", "dllm_qgemm_planned", "dllm_lmhead_planned", "dllm_qgemm_noalloc",
+    "dllm_qgemm_pair_workspace_bytes", "dllm_qgemm_pair",
 )
 
 # tile configurations of dllm_qgemm_planned and the super-block sums export
@@ -70,6 +71,8 @@ def _load():
         "dllm_qgemm_planned": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P, I64, I, I, P]),
         "dllm_lmhead_planned": (I, [I, P, I64, I64, P, I64, I64, P, I64, P, I64, P, P, P, P, I64, I, P]),
         "dllm_qgemm_noalloc": (I, [I, P, I64, I64, P, P, I64, P, P, I64, P]),
+        "dllm_qgemm_pair_workspace_bytes": (I64, [I, I64, I, I64, I64, I64]),
+        "dllm_qgemm_pair": (I, [I, P, I64, P, P, I64, I, P, I64, P, P, I64, I64, P, P, I64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -224,6 +227,32 @@ def qgemm(qtype: int, w: torch.Tensor, N: int, K: int, x_q8k: torch.Tensor, M: i
         _check(lib.dllm_qgemm_bias(qtype, _ptr(w), N, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(bias), _ptr(y),
                                    y.stride(0), _ptr(workspace), wsb, _stream(dev)))
     return y
+
+
+def qgemm_pair_workspace_bytes(qtype_a: int, N_a: int, qtype_b: int, N_b: int, K: int, M: int) -> int:
+    return int(lib.dllm_qgemm_pair_workspace_bytes(qtype_a, N_a, qtype_b, N_b, K, M))
+
+
+def qgemm_pair(a: tuple, b: tuple, K: int, x_q8k: torch.Tensor, M: int,
+               workspace: torch.Tensor | None = None, x_dmax: torch.Tensor | None = None):
+    """Two GEMMs of one activation matrix in one call (dllm_qgemm_pair).
+    a and b are (qtype, w, N, y, bias) with y (f32 [M, >= N], row-strided
+    views allowed) and bias (f32 [N]) optional (None); returns (y_a, y_b)."""
+    outs, args = [], []
+    for qtype, w, N, y, bias in (a, b):
+        dev = _dev(w)
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        assert y.dtype == torch.float32 and y.stride(1) == 1
+        if bias is not None:
+            assert bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() >= N
+        outs.append(y)
+        args += [qtype, _ptr(w), N, _ptr(bias), _ptr(y), y.stride(0)]
+    if x_dmax is not None:
+        assert x_dmax.dtype == torch.float32 and x_dmax.is_contiguous() and x_dmax.numel() >= M
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dllm_qgemm_pair(*args, K, _ptr(x_q8k), _ptr(x_dmax), M, _ptr(workspace), wsb, _stream(_dev(x_q8k))))
+    return outs[0], outs[1]
 
 
 def lmhead_workspace_bytes(qtype: int, N: int, K: int, n_rows: int) -> int:

@@ -204,11 +204,13 @@ int64_t split_workspace_bytes(const Plan& pl, int64_t M, int64_t N) {
   return pl.S > 1 ? kCounterBytes + (int64_t)pl.S * M * split_ld(N) * 4 : 0;
 }
 
-// Launch a planned GEMM: y directly, or the split partials in the workspace
-// with their reduction fused into the same kernel.
-int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
-             const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
-             hipStream_t s) {
+dim3 plan_grid(const Plan& pl) { return dim3((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles); }
+
+// The kernel parameters of a planned GEMM: y directly, or with a K split the
+// partial slices at `slices` and one arrival counter per output tile from
+// `counters` on, the reduction fused into the same kernel.
+GemmParams plan_params(const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k, const float* x_dmax,
+                       int64_t M, const float* bias, float* y, int64_t ldy, uint32_t* counters, float* slices) {
   GemmParams p{};
   p.w = (const uint8_t*)w;
   p.xq = (const uint8_t*)x_q8k;
@@ -217,21 +219,30 @@ int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N
   p.SB = K / 256;
   p.M = M;
   p.sps = pl.sps;
-  const dim3 grid((unsigned)pl.n_tiles, (unsigned)pl.S, (unsigned)pl.m_tiles);
   if (pl.S == 1) {
     p.out = y;
     p.ldo = ldy;
     p.bias = bias;
   } else {
-    p.out = (float*)((uint8_t*)workspace + kCounterBytes);
+    p.out = slices;
     p.ldo = split_ld(N);
     p.split_stride = M * p.ldo;
-    p.tile_cnt = (uint32_t*)workspace;
+    p.tile_cnt = counters;
     p.red_y = y;
     p.red_ldy = ldy;
     p.red_bias = bias;  // added once, by the reduction
   }
-  return hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, grid, false, s), fn);
+  return p;
+}
+
+// Launch a planned GEMM (a split's counters at the start of the workspace,
+// its partial slices after them).
+int run_plan(const char* fn, int qtype, const Plan& pl, const void* w, int64_t N, int64_t K, const void* x_q8k,
+             const float* x_dmax, int64_t M, const float* bias, float* y, int64_t ldy, void* workspace,
+             hipStream_t s) {
+  const GemmParams p = plan_params(pl, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, (uint32_t*)workspace,
+                                   (float*)((uint8_t*)workspace + kCounterBytes));
+  return hip_status(launch_qgemm(qtype, p, pl.tb, pl.cfg, plan_grid(pl), false, s), fn);
 }
 
 }  // namespace
@@ -371,6 +382,79 @@ int dllm_qgemm_bias(int qtype, const void* w, int64_t N, int64_t K, const void* 
                     void* stream) {
   return qgemm_impl("dllm_qgemm_bias", qtype, w, N, K, x_q8k, x_dmax, M, bias, y, ldy, workspace, workspace_bytes,
                     stream);
+}
+
+// ---- dllm_qgemm_pair: two GEMMs of one activation matrix, one launch -----
+
+namespace {
+// Workspace of a pair: the counters (A's tiles first, then B's), A's slices,
+// B's slices.  Without a split on either side, none.
+struct PairPlan {
+  Plan a, b;
+  int64_t cnt_b;           // B's first counter
+  int64_t slices_a_bytes;  // bytes of A's slices (0 unsplit)
+  int64_t need;            // workspace bytes
+};
+int64_t split_slice_bytes(const Plan& pl, int64_t M, int64_t N) {
+  return pl.S > 1 ? (int64_t)pl.S * M * split_ld(N) * 4 : 0;
+}
+PairPlan plan_pair(int qa, int64_t Na, int qb, int64_t Nb, int64_t K, int64_t M, bool allow_split) {
+  PairPlan pp{};
+  pp.a = plan_gemm(qa, Na, K, M, allow_split);
+  pp.b = plan_gemm(qb, Nb, K, M, allow_split);
+  pp.cnt_b = pp.a.S > 1 ? pp.a.n_tiles * pp.a.m_tiles : 0;
+  // both splits' counters must fit the counter region; B's shifts after A's
+  if (pp.b.S > 1 && pp.cnt_b + pp.b.n_tiles * pp.b.m_tiles > kMaxSplitTiles) pp.cnt_b = 0;
+  pp.slices_a_bytes = split_slice_bytes(pp.a, M, Na);
+  const int64_t sb = split_slice_bytes(pp.b, M, Nb);
+  pp.need = (pp.slices_a_bytes + sb) > 0 ? kCounterBytes + pp.slices_a_bytes + sb : 0;
+  return pp;
+}
+}  // namespace
+
+int64_t dllm_qgemm_pair_workspace_bytes(int qtype_a, int64_t N_a, int qtype_b, int64_t N_b, int64_t K, int64_t M) {
+  if (check_qtype(qtype_a) || check_qtype(qtype_b) || N_a <= 0 || N_b <= 0 || M <= 0 || K <= 0 || K % 256) return -1;
+  return plan_pair(qtype_a, N_a, qtype_b, N_b, K, M, true).need;
+}
+
+int dllm_qgemm_pair(int qtype_a, const void* w_a, int64_t N_a, const float* bias_a, float* y_a, int64_t ldy_a,
+                    int qtype_b, const void* w_b, int64_t N_b, const float* bias_b, float* y_b, int64_t ldy_b,
+                    int64_t K, const void* x_q8k, const float* x_dmax, int64_t M, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+  const char* fn = "dllm_qgemm_pair";
+  int rc = check_gemm_args(fn, qtype_a, w_a, N_a, K, x_q8k, M);
+  if (rc) return rc;
+  if ((rc = check_gemm_args(fn, qtype_b, w_b, N_b, K, x_q8k, M))) return rc;
+  if (!y_a || !y_b) return fail(DLLM_E_ARG, "%s: null output pointer (y_a=%p, y_b=%p)", fn, (void*)y_a, (void*)y_b);
+  if (ldy_a < N_a || ldy_b < N_b)
+    return fail(DLLM_E_ARG, "%s: need ldy_a >= N_a and ldy_b >= N_b (ldy_a=%lld, N_a=%lld, ldy_b=%lld, N_b=%lld)", fn,
+                (long long)ldy_a, (long long)N_a, (long long)ldy_b, (long long)N_b);
+  if (!aligned(y_a, 4) || !aligned(y_b, 4) || !aligned(x_dmax, 4) || !aligned(bias_a, 4) || !aligned(bias_b, 4))
+    return fail(DLLM_E_ALIGN, "%s: y_a, y_b, x_dmax and the biases must be 4-byte aligned", fn);
+  PairPlan pp = plan_pair(qtype_a, N_a, qtype_b, N_b, K, M, true);
+  if (pp.need > 0 && (!workspace || workspace_bytes < pp.need || !aligned(workspace, 16)))
+    pp = plan_pair(qtype_a, N_a, qtype_b, N_b, K, M, false);  // no usable workspace: no split on either side
+  // (a plan without a split uses neither counters nor slices)
+  uint8_t* const ws = pp.need > 0 ? (uint8_t*)workspace : nullptr;
+  uint32_t* const cnt_a = ws ? (uint32_t*)ws : nullptr;
+  uint32_t* const cnt_b = ws ? (uint32_t*)ws + pp.cnt_b : nullptr;
+  float* const slices_a = ws ? (float*)(ws + kCounterBytes) : nullptr;
+  float* const slices_b = ws ? (float*)(ws + kCounterBytes + pp.slices_a_bytes) : nullptr;
+  const GemmParams pa = plan_params(pp.a, w_a, N_a, K, x_q8k, x_dmax, M, bias_a, y_a, ldy_a, cnt_a, slices_a);
+  const GemmParams pb = plan_params(pp.b, w_b, N_b, K, x_q8k, x_dmax, M, bias_b, y_b, ldy_b, cnt_b, slices_b);
+  const hipStream_t s = (hipStream_t)stream;
+  const bool counters_apart = pp.b.S == 1 || pp.a.S == 1 || pp.cnt_b > 0;
+  const int64_t wgs = pp.a.n_tiles * pp.a.S * pp.a.m_tiles + pp.b.n_tiles * pp.b.S * pp.b.m_tiles;
+  if (counters_apart && wgs + 16 < 0x7fffffffLL &&
+      qgemm_pair_fits(qtype_a, pp.a.cfg, pp.a.tb, qtype_b, pp.b.cfg, pp.b.tb))
+    return hip_status(launch_qgemm_pair(qtype_a, pa, pp.a.tb, pp.a.cfg, plan_grid(pp.a), qtype_b, pb, pp.b.tb,
+                                        pp.b.cfg, plan_grid(pp.b), s),
+                      fn);
+  // no grouped kernel for these two plans: the two launches in order on the
+  // stream (the second may then reuse the first one's counters)
+  rc = hip_status(launch_qgemm(qtype_a, pa, pp.a.tb, pp.a.cfg, plan_grid(pp.a), false, s), fn);
+  if (rc) return rc;
+  return hip_status(launch_qgemm(qtype_b, pb, pp.b.tb, pp.b.cfg, plan_grid(pp.b), false, s), fn);
 }
 
 // ---- dllm_qgemm_noalloc: the K split in memory the library holds --------

@@ -64,6 +64,13 @@ hipError_t launch_decode_qk(int qtype, const uint8_t* w, int64_t nsb, uint8_t* o
 int qgemm_cfg_rows(int cfg);
 int qgemm_cfg_max_tb(int cfg);
 hipError_t launch_qgemm(int qtype, const GemmParams& p, int tb, int cfg, dim3 grid, bool argmax, hipStream_t s);
+// Two planned GEMMs of one activation matrix in one launch, their
+// work-groups interleaved over one grid (each tile computes what it computes
+// in its own launch); qgemm_pair_fits says which pairs of (type, cfg, token
+// tile) have a grouped kernel.
+bool qgemm_pair_fits(int qtype_a, int cfg_a, int tb_a, int qtype_b, int cfg_b, int tb_b);
+hipError_t launch_qgemm_pair(int qtype_a, const GemmParams& pa, int tb_a, int cfg_a, dim3 grid_a, int qtype_b,
+                             const GemmParams& pb, int tb_b, int cfg_b, dim3 grid_b, hipStream_t s);
 // The same kernels in their test form: the exact int32 super-block sums
 // A[m][n][sb] go to p.out instead of y; token tile qgemm_cfg_max_tb(cfg).
 hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s);

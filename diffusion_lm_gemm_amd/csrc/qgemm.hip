@@ -124,65 +124,127 @@ __device__ __forceinline__ void sum_split_tile(const GemmParams& p, int64_t row_
 // reads zeros and makes no memory access.
 constexpr uint32_t kNoLoad = 0x80000000u;
 
-// SUMS: the test form of the same kernel, which also stores every tile's
-// exact int32 super-block sums A_sb = (hi << shift) + lo, as formed for the
-// epilogue, to ((int32_t*)p.out)[(m * N + n) * SB + sb], and writes no y.
-template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
+// The LDS a work-group of one tile configuration uses (sizes of its arrays).
+//  * The activation stage: the int8 quants of TOKP tokens (TOK padded so the
+//    buffer-to-LDS loads fill it exactly; the padding rows are loaded and
+//    never read).  Two stages (double buffer) are separate objects: where each
+//    step names them directly the compiler sees that the buffer-to-LDS loads
+//    filling one stage do not alias the reads of the other, and does not wait
+//    for those loads before the reads.  One stage (ST = 1) is the first
+//    object, or with SPLIT both, tokens [0, H) in the first and the rest in
+//    the second (so that both forms fit the same arrays in a grouped kernel).
+//  * d_x staging: items (a token, or for Q4_K a (token, half q) pair that
+//    covers sub-blocks 4q .. 4q+3) are spread over the loading threads.
+//    Token t's d_x sits at slot t (written by its item with q = 0); every
+//    other item writes a slot of its own past TOK, which nothing reads, so
+//    every store is unconditional and has its own address.  DXS floats per
+//    stage.
+//  * Q4_K: an 8-slot ring (two groups of four super-blocks) of min-term
+//    activation operands, high halves [slot][token][8] f16 then low halves
+//    likewise: one group is read while the next is written.  A lane's 16-byte
+//    read of one token's eight values has consecutive tokens at consecutive
+//    16-byte slots, so the reads of a wave hit distinct banks.
+//  * the per-token pre-scale, and the argmax epilogue's keys and statistics.
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST, bool SPLIT = false>
+struct QgemmLds {
+  static constexpr bool ONE = (ST == 1);
+  static constexpr bool MINS = (QT == QT_Q4K);
+  static constexpr int TOK = TB * 16;  // tokens per work-group (MFMA columns)
+  // Stage loads and d_x items are issued by the first LW waves only: with
+  // two or more waves per SIMD the others then start each step on the matrix
+  // cores instead of queueing behind the first ones' loads.
+  static constexpr int LW = (!ONE && RB == 1 && NW >= 8) ? 4 : NW;
+  static constexpr int TOKP = (TOK + 4 * LW - 1) / (4 * LW) * (4 * LW);
+  static constexpr int H = (ONE && SPLIT) ? 16 * ((TB + 1) / 2) : TOKP;
+  static constexpr int ACT0 = H * ACT_ROW;
+  static constexpr int ACT1 = ONE ? (TOKP > H ? (TOKP - H) * ACT_ROW : 16) : TOKP * ACT_ROW;
+  static constexpr bool SPLIT1 = ONE && TOKP > H;  // the one stage spans both arrays
+  static constexpr int NTHL = 64 * LW;
+  static constexpr int NITEM = MINS ? TOK * 2 : TOK;
+  static constexpr int IPT = (NITEM + NTHL - 1) / NTHL;  // items per loading thread
+  static constexpr int DXS = TOK + IPT * NTHL;
+  static constexpr int DX = (ONE ? 1 : 2) * DXS;
+  static constexpr int AMS = 8;                    // halves per token record of the ring
+  static constexpr int RSLOTS = ONE ? 4 : 8;       // ring slots (one group, or two)
+  static constexpr int AMLO = RSLOTS * TOK * AMS;  // offset of the low halves
+  static constexpr int AMIN = MINS ? 2 * AMLO + 8 * (IPT * NTHL - NITEM) + 8 : 8;
+  static constexpr int KEYS = ARGMAX ? NW * TOK : 1;
+};
+
+// The LDS arrays of a work-group (at least the QgemmLds sizes), given by the
+// kernel that declares them.
+struct QgemmSmem {
+  uint8_t* act0;
+  uint8_t* act1;
+  float* dx;
+  float* esc;
+  _Float16* amin;
+  uint64_t* key;
+  float2* stat;
+  int* last;
+};
+
+// Which tile a work-group computes: (bx, by, bz) of a (gx, gy, *) grid of
+// row tiles, K splits and token tiles.  HwTile: the work-group's own place in
+// its grid; WgTile: a place given by the kernel.
+struct HwTile {
+  __device__ uint32_t bx() const { return blockIdx.x; }
+  __device__ uint32_t by() const { return blockIdx.y; }
+  __device__ uint32_t bz() const { return blockIdx.z; }
+  __device__ uint32_t gx() const { return gridDim.x; }
+  __device__ uint32_t gy() const { return gridDim.y; }
+};
+struct WgTile {
+  uint32_t x, y, z, nx, ny;
+  __device__ uint32_t bx() const { return x; }
+  __device__ uint32_t by() const { return y; }
+  __device__ uint32_t bz() const { return z; }
+  __device__ uint32_t gx() const { return nx; }
+  __device__ uint32_t gy() const { return ny; }
+};
+
+// One work-group of the GEMM: tile t.
+// SUMS: the test form, which also stores every tile's exact int32
+// super-block sums A_sb = (hi << shift) + lo, as formed for the epilogue, to
+// ((int32_t*)p.out)[(m * N + n) * SB + sb], and writes no y.
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST, bool SUMS, bool SPLIT, class TILE>
+__device__ __forceinline__ void qgemm_wg(const GemmParams p, const TILE wt, const QgemmSmem lds) {
   static_assert(NW == 4 || NW == 8 || NW == 12, "waves per work-group: 4, 8 or 12 (whole SIMDs)");
+  static_assert(ST == 2 || NW == 4, "one activation stage: four waves");
+  using G = QgemmLds<QT, TB, NW, RB, ARGMAX, ST, SPLIT>;
   constexpr bool ONE = (ST == 1);
-  constexpr int TOK = TB * 16;          // tokens per work-group (MFMA columns)
+  constexpr int TOK = G::TOK;
   constexpr int NTH = 64 * NW;          // threads
   constexpr int ROWS = 16 * RB * NW;    // weight rows per work-group
   constexpr int SHIFT = QTr<QT>::SHIFT;
   constexpr int BYTES = QTr<QT>::BYTES;
   constexpr int RAW = QTr<QT>::RAW;
-  constexpr bool MINS = (QT == QT_Q4K);
-  // Stage loads and d_x items are issued by the first LW waves only: with
-  // two or more waves per SIMD the others then start each step on the matrix
-  // cores instead of queueing behind the first ones' loads.
-  constexpr int LW = (!ONE && RB == 1 && NW >= 8) ? 4 : NW;
+  constexpr bool MINS = G::MINS;
+  constexpr int LW = G::LW;
+  constexpr int NTHL = G::NTHL;
   // buffer-to-LDS loads per loading wave per stage: 16 units per token, 64
-  // units per wave-wide load; the stage is padded to TOKP rows so the loads
-  // fill it exactly (the padding rows are loaded and never read).
-  constexpr int TOKP = (TOK + 4 * LW - 1) / (4 * LW) * (4 * LW);
-  constexpr int NTHL = 64 * LW;
-  constexpr int DPW = TOKP * 16 / (64 * LW);
-  // Two activation stages (double buffer), their d_x, and for Q4_K an 8-slot
-  // ring (two groups of four super-blocks) of min-term activation operands,
-  // high halves [slot][token][8] f16 then low halves likewise: one group is
-  // read while the next is written.  A lane's 16-byte read of one token's
-  // eight values has consecutive tokens at consecutive 16-byte slots, so the
-  // reads of a wave hit distinct banks.
-  // The two stages are separate objects.  Where each step names them directly
-  // the compiler sees that the buffer-to-LDS loads filling one stage do not
-  // alias the reads of the other, and does not wait for those loads before
-  // the reads.
-  __shared__ __attribute__((aligned(16))) uint8_t s_act0[TOKP * ACT_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_act1[ONE ? 16 : TOKP * ACT_ROW];
-  constexpr int AMS = 8;                    // halves per token record of the ring
-  constexpr int RSLOTS = ONE ? 4 : 8;       // ring slots (one group, or two)
-  constexpr int AMLO = RSLOTS * TOK * AMS;  // offset of the low halves
-  // d_x staging: items (a token, or for Q4_K a (token, half q) pair that
-  // covers sub-blocks 4q .. 4q+3) are spread over all threads.  Token t's d_x
-  // sits at slot t (written by its item with q = 0); every other item writes
-  // a slot of its own past TOK, which nothing reads, so every store is
-  // unconditional and has its own address.
-  constexpr int NITEM = MINS ? TOK * 2 : TOK;
-  constexpr int IPT = (NITEM + NTHL - 1) / NTHL;  // items per thread
-  __shared__ float s_dx[ONE ? 1 : 2][TOK + IPT * NTHL];
-  __shared__ float s_esc[TOK];
-  __shared__ __attribute__((aligned(16))) _Float16 s_amin[MINS ? 2 * AMLO + 8 * (IPT * NTHL - NITEM) + 8 : 8];
-  __shared__ uint64_t s_key[ARGMAX ? NW * TOK : 1];
-  __shared__ float2 s_stat[ARGMAX ? NW * TOK : 1];
+  // units per wave-wide load
+  constexpr int DPW = G::TOKP * 16 / (64 * LW);
+  constexpr int AMS = G::AMS;
+  constexpr int AMLO = G::AMLO;
+  constexpr int NITEM = G::NITEM;
+  constexpr int IPT = G::IPT;
+  constexpr int DXS = G::DXS;
+  uint8_t* const s_act0 = lds.act0;
+  uint8_t* const s_act1 = lds.act1;
+  float* const s_dx = lds.dx;
+  float* const s_esc = lds.esc;
+  _Float16* const s_amin = lds.amin;
+  uint64_t* const s_key = lds.key;
+  float2* const s_stat = lds.stat;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int64_t N = p.N, SB = p.SB, M = p.M;
-  const int64_t m0 = (int64_t)blockIdx.z * TOK;
-  const int64_t s0 = (int64_t)blockIdx.y * p.sps;
+  const int64_t m0 = (int64_t)wt.bz() * TOK;
+  const int64_t s0 = (int64_t)wt.by() * p.sps;
   const int64_t s1 = (s0 + p.sps < SB) ? s0 + p.sps : SB;
-  const int64_t row0 = (int64_t)blockIdx.x * ROWS + wv * 16 * RB;  // first row of this wave
+  const int64_t row0 = (int64_t)wt.bx() * ROWS + wv * 16 * RB;  // first row of this wave
   // Buffer resources: loads past num_records read as zero (rows >= N,
   // tokens >= M).  The host keeps both operands below 2 GiB.
   const rsrc_t wr = make_rsrc(p.w, N * SB * BYTES);
@@ -227,10 +289,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     const uint32_t soff = (uint32_t)(sb * Q8K_BYTES);
 #pragma unroll
     for (int k = 0; k < DPW; ++k) {
-      const int tok = (wv * DPW + k) * 4 + (lane >> 4);
+      const int j = wv * DPW + k;  // LDS units 64 j .. 64 j + 63: tokens 4 j .. 4 j + 3
+      const int tok = j * 4 + (lane >> 4);
       const uint32_t voff = dma_tok0 + k * tok_step + 16 * ((lane & 15) ^ (tok & 15));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(stage + (wv * DPW + k) * 1024), 16, voff, soff, 0, 0);
+      uint8_t* dst;
+      if constexpr (G::SPLIT1) dst = (4 * j < G::H) ? s_act0 + j * 1024 : s_act1 + (j - G::H / 4) * 1024;
+      else if constexpr (ONE) dst = s_act0 + j * 1024;
+      else dst = stage + j * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0,
+                                               0);
     }
   };
   // idx_b: Q4_K bsum pairs (2j, 2j+1) for j = 4q .. 4q+3, one per dword
@@ -261,10 +328,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       const int it_c = live ? item : NITEM - 1;
       const int tok = MINS ? (it_c >> 1) : it_c;
       const float dx = __builtin_bit_cast(float, idx_d[k]) * s_esc[tok];
-      if constexpr (!MINS) s_dx[buf][item] = dx;
+      if constexpr (!MINS) s_dx[buf * DXS + item] = dx;
       if constexpr (MINS) {
         const int q = it_c & 1;
-        s_dx[buf][(live && q == 0) ? tok : TOK + item] = dx;
+        s_dx[buf * DXS + ((live && q == 0) ? tok : TOK + item)] = dx;
         // activation side of the min term: d_x * (bsum_{2j} + bsum_{2j+1})
         // for j = 4q .. 4q+3, as f16 high and low halves
         typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -310,7 +377,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     const int slot = it & 3;
     const bool more = sb + 1 < s1;
     if constexpr (ONE) {
-      act_dma(s_act0, sb);
+      act_dma(nullptr, sb);
       items_load(sb);
     } else {
       act_dma(act_next, sb + 1);  // past the end: an unread stage
@@ -351,13 +418,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
 #pragma unroll
     for (int c = 0; c < 4; ++c) bunit[c] = 16 * (act_unit<QT>(c, g4) ^ r);  // token t*16 + r has (tok & 15) == r
     auto loadB = [&](int t, v4i(&dstB)[4]) {
-      const uint8_t* arow = act + (t * 16 + r) * ACT_ROW;
+      const uint8_t* arow;
+      if constexpr (G::SPLIT1)
+        arow = (t * 16 < G::H) ? s_act0 + (t * 16 + r) * ACT_ROW : s_act1 + (t * 16 - G::H + r) * ACT_ROW;
+      else if constexpr (ONE) arow = s_act0 + (t * 16 + r) * ACT_ROW;
+      else arow = act + (t * 16 + r) * ACT_ROW;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dstB[c] = *(const v4i*)(arow + bunit[c]);
     };
     auto flush = [&](int t, int b, const v4i& al, const v4i& ah) {
       sums_store(t, b, sb, al, ah);
-      const float dx = s_dx[buf][t * 16 + r];
+      const float dx = s_dx[buf * DXS + t * 16 + r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = (ah[i] << SHIFT) + al[i];
@@ -481,7 +552,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
     };
     float dxr[TB];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) dxr[t] = s_dx[buf][t * 16 + r];
+    for (int t = 0; t < TB; ++t) dxr[t] = s_dx[buf * DXS + t * 16 + r];
     auto flush = [&](int t, const v4i& al, const v4i& ah) {
       sums_store(t, 0, sb, al, ah);
 #pragma unroll
@@ -626,7 +697,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   }
 
   if constexpr (ONE) {
-    for (int64_t sb = s0; sb < s1; ++sb) step(sb, s_act0, s_act0, 0);
+    for (int64_t sb = s0; sb < s1; ++sb) step(sb, nullptr, nullptr, 0);
   } else if constexpr (RB == 1) {
     // the first block is unpacked here (and its min-term bytes kept); then
     // two steps per iteration, each naming its stages and weights directly
@@ -657,11 +728,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   // (plus the bias of those rows, when given: only without a K split, whose
   // reduction adds it instead)
   if constexpr (SUMS) return;
-  float* outp = p.out + (int64_t)blockIdx.y * p.split_stride;
+  float* outp = p.out + (int64_t)wt.by() * p.split_stride;
   // K split with the reduction fused: the slice [M][ldo] goes out with
   // device-coherent 16-byte stores (ldo a multiple of 64 >= N, so every
   // group of four rows that starts inside N is whole)
-  const rsrc_t wsr = make_rsrc(p.out, p.tile_cnt ? (int64_t)gridDim.y * p.split_stride * 4 : 0);
+  const rsrc_t wsr = make_rsrc(p.out, p.tile_cnt ? (int64_t)wt.gy() * p.split_stride * 4 : 0);
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int64_t nbase = row0 + 16 * b + 4 * g4;
@@ -679,7 +750,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       yacc[b][t] = yv;
       if (p.tile_cnt) {
         if (m < M && nbase < N)
-          buf_st128_dev(wsr, (uint32_t)(((int64_t)blockIdx.y * p.split_stride + m * p.ldo + nbase) * 4),
+          buf_st128_dev(wsr, (uint32_t)(((int64_t)wt.by() * p.split_stride + m * p.ldo + nbase) * 4),
                         __builtin_bit_cast(v4u, yv));
       } else if (m < M) {
         float* dst = outp + m * p.ldo + nbase;
@@ -700,23 +771,23 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
   if (p.tile_cnt) {
     // K split with the reduction fused: once this work-group's slice has
     // reached memory (each wave waits for its own stores), it is counted in
-    // with a device-scope atomic; the last of the tile's gridDim.y
+    // with a device-scope atomic; the last of the tile's gy
     // work-groups to arrive sums the slices.  That last arrival also resets
     // the counter, so the next call on the stream finds it 0.  The slices
     // are written and read with device-coherent accesses, so no cache
     // maintenance is needed on either side.
-    __shared__ int s_last;
+    int* const s_last = lds.last;
     wait_vmem();
     __syncthreads();
     if (tid == 0) {
-      uint32_t* c = p.tile_cnt + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+      uint32_t* c = p.tile_cnt + (int64_t)wt.bz() * wt.gx() + wt.bx();
       const uint32_t before = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = (before + 1 == gridDim.y);
+      const bool last = (before + 1 == wt.gy());
       if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last ? 1 : 0;
+      *s_last = last ? 1 : 0;
     }
     __syncthreads();
-    if (s_last) sum_split_tile<ROWS, TOK, NTH>(p, (int64_t)blockIdx.x * ROWS, m0, (int)gridDim.y, tid);
+    if (*s_last) sum_split_tile<ROWS, TOK, NTH>(p, (int64_t)wt.bx() * ROWS, m0, (int)wt.gy(), tid);
   }
 
   if constexpr (ARGMAX) {
@@ -760,15 +831,86 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1)
       uint64_t best = s_key[tid];
 #pragma unroll
       for (int k = 1; k < NW; ++k) best = s_key[k * TOK + tid] > best ? s_key[k * TOK + tid] : best;
-      if (m < M) p.keys[(int64_t)blockIdx.x * M + m] = best;
+      if (m < M) p.keys[(int64_t)wt.bx() * M + m] = best;
       if (p.stats) {
         float sm = s_stat[tid].x, ss = s_stat[tid].y;
 #pragma unroll
         for (int k = 1; k < NW; ++k) softmax_merge(sm, ss, s_stat[k * TOK + tid].x, s_stat[k * TOK + tid].y);
-        if (m < M) p.stats[(int64_t)blockIdx.x * M + m] = float2{sm, ss};
+        if (m < M) p.stats[(int64_t)wt.bx() * M + m] = float2{sm, ss};
       }
     }
   }
+}
+
+// The LDS arrays of a kernel: one set per instantiation of the sizes (the
+// largest of its configurations' for a kernel that runs several).
+template <int A0, int A1, int DX, int ESC, int AMIN, int KEYS>
+__device__ __forceinline__ QgemmSmem qgemm_lds() {
+  __shared__ __attribute__((aligned(16))) uint8_t s_act0[A0];
+  __shared__ __attribute__((aligned(16))) uint8_t s_act1[A1];
+  __shared__ float s_dx[DX];
+  __shared__ float s_esc[ESC];
+  __shared__ __attribute__((aligned(16))) _Float16 s_amin[AMIN];
+  __shared__ uint64_t s_key[KEYS];
+  __shared__ float2 s_stat[KEYS];
+  __shared__ int s_last;
+  return QgemmSmem{s_act0, s_act1, s_dx, s_esc, s_amin, s_key, s_stat, &s_last};
+}
+
+template <int QT, int TB, int NW, int RB, bool ARGMAX, int ST = 2, bool SUMS = false>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && (TB <= 5 || ST == 1)) ? 2 : 1) void k_qgemm(GemmParams p) {
+  using G = QgemmLds<QT, TB, NW, RB, ARGMAX, ST>;
+  const QgemmSmem lds = qgemm_lds<G::ACT0, G::ACT1, G::DX, G::TOK, G::AMIN, G::KEYS>();
+  qgemm_wg<QT, TB, NW, RB, ARGMAX, ST, SUMS, false>(p, HwTile{}, lds);
+}
+
+// Two GEMMs over the same activations in one launch (a grouped launch): the
+// work-groups of A's grid and of B's grid, both four-wave tiles that fit two
+// work-groups per CU, share one grid, so that a CU holds a work-group of each
+// where either launch alone would leave it half used.  Blocks go in groups
+// of eight (one per XCD, in dispatch order), alternating A and B while both
+// have groups left; a work-group's index in its own grid keeps its place
+// modulo 8, so each tile runs on the XCD it would have run on alone.  Every
+// tile computes exactly what it computes in its own launch.
+struct PairGrid {
+  int64_t n[2];       // work-groups of A's and B's grid
+  int64_t gx[2], gy[2];
+  int64_t groups[2];  // groups of eight blocks: cdiv(n, 8)
+};
+
+template <int Q, int TB, int ST>
+struct Cfg4 {  // a four-wave, one-row-block tile configuration (one stage split over both arrays)
+  static constexpr int QT = Q, T = TB, S = ST;
+  using G = QgemmLds<Q, TB, 4, 1, false, ST, true>;
+};
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <class CA, class CB>
+__global__ __launch_bounds__(256, 2) void k_qgemm_pair(GemmParams pa, GemmParams pb, PairGrid g) {
+  using GA = typename CA::G;
+  using GB = typename CB::G;
+  const QgemmSmem lds = qgemm_lds<cmax(GA::ACT0, GB::ACT0), cmax(GA::ACT1, GB::ACT1), cmax(GA::DX, GB::DX),
+                                  cmax(GA::TOK, GB::TOK), cmax(GA::AMIN, GB::AMIN), 1>();
+  const int64_t grp = blockIdx.x >> 3, k = blockIdx.x & 7;
+  const int64_t both = g.groups[0] < g.groups[1] ? g.groups[0] : g.groups[1];
+  int which;
+  int64_t gi;
+  if (grp < 2 * both) {
+    which = (int)(grp & 1);
+    gi = grp >> 1;
+  } else {
+    which = g.groups[0] > g.groups[1] ? 0 : 1;
+    gi = grp - both;
+  }
+  const int64_t li = gi * 8 + k;  // index in that GEMM's own grid
+  if (li >= g.n[which]) return;   // the tail of a partial group (whole work-group)
+  const int64_t gx = g.gx[which], gy = g.gy[which];
+  const int64_t rest = li / gx;
+  const WgTile wt{(uint32_t)(li - rest * gx), (uint32_t)(rest % gy), (uint32_t)(rest / gy), (uint32_t)gx,
+                  (uint32_t)gy};
+  if (which == 0) qgemm_wg<CA::QT, CA::T, 4, 1, false, CA::S, false, true>(pa, wt, lds);
+  else qgemm_wg<CB::QT, CB::T, 4, 1, false, CB::S, false, true>(pb, wt, lds);
 }
 
 // argmax[m] = lowest row index of the largest logit, from per-tile keys.
@@ -926,6 +1068,51 @@ static hipError_t launch_sums_cfg(const GemmParams& p, int cfg, dim3 grid, hipSt
 hipError_t launch_qgemm_sums(int qtype, const GemmParams& p, int cfg, dim3 grid, hipStream_t s) {
   if (qtype == QT_Q4K) return launch_sums_cfg<QT_Q4K>(p, cfg, grid, s);
   return launch_sums_cfg<QT_Q6K>(p, cfg, grid, s);
+}
+
+// The grouped pairs that have a kernel: a Q4_K configuration-6 tile of 80
+// tokens with a Q6_K tile of configuration 5 (160 tokens) or 6 (80 tokens);
+// A and B in either order.
+namespace {
+using PairQ4c6 = Cfg4<QT_Q4K, 5, 2>;
+using PairQ6c5 = Cfg4<QT_Q6K, 10, 1>;
+using PairQ6c6 = Cfg4<QT_Q6K, 5, 2>;
+
+int pair_kind(int qa, int cfg_a, int tb_a, int qb, int cfg_b, int tb_b) {
+  if (qa != QT_Q4K || cfg_a != 6 || tb_a != 5 || qb != QT_Q6K) return 0;
+  if (cfg_b == 5 && tb_b == 10) return 1;
+  if (cfg_b == 6 && tb_b == 5) return 2;
+  return 0;
+}
+}  // namespace
+
+bool qgemm_pair_fits(int qtype_a, int cfg_a, int tb_a, int qtype_b, int cfg_b, int tb_b) {
+  return pair_kind(qtype_a, cfg_a, tb_a, qtype_b, cfg_b, tb_b) != 0 ||
+         pair_kind(qtype_b, cfg_b, tb_b, qtype_a, cfg_a, tb_a) != 0;
+}
+
+hipError_t launch_qgemm_pair(int qtype_a, const GemmParams& pa, int tb_a, int cfg_a, dim3 grid_a, int qtype_b,
+                             const GemmParams& pb, int tb_b, int cfg_b, dim3 grid_b, hipStream_t s) {
+  const bool swap = pair_kind(qtype_a, cfg_a, tb_a, qtype_b, cfg_b, tb_b) == 0;
+  const int kind = swap ? pair_kind(qtype_b, cfg_b, tb_b, qtype_a, cfg_a, tb_a)
+                        : pair_kind(qtype_a, cfg_a, tb_a, qtype_b, cfg_b, tb_b);
+  if (kind == 0) return hipErrorInvalidValue;
+  const GemmParams& p0 = swap ? pb : pa;
+  const GemmParams& p1 = swap ? pa : pb;
+  const dim3 g0 = swap ? grid_b : grid_a, g1 = swap ? grid_a : grid_b;
+  PairGrid g{};
+  g.n[0] = (int64_t)g0.x * g0.y * g0.z;
+  g.n[1] = (int64_t)g1.x * g1.y * g1.z;
+  g.gx[0] = g0.x;
+  g.gy[0] = g0.y;
+  g.gx[1] = g1.x;
+  g.gy[1] = g1.y;
+  g.groups[0] = (g.n[0] + 7) / 8;
+  g.groups[1] = (g.n[1] + 7) / 8;
+  const dim3 grid((unsigned)(8 * (g.groups[0] + g.groups[1])));
+  if (kind == 1) hipLaunchKernelGGL((k_qgemm_pair<PairQ4c6, PairQ6c5>), grid, dim3(256), 0, s, p0, p1, g);
+  else hipLaunchKernelGGL((k_qgemm_pair<PairQ4c6, PairQ6c6>), grid, dim3(256), 0, s, p0, p1, g);
+  return hipGetLastError();
 }
 
 int qgemm_cfg_rows(int cfg) {

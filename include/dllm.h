@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DLLM_ABI_VERSION 10
+#define DLLM_ABI_VERSION 11
 
 /* qtype tags: the GGUF tensor-type ids. */
 #define DLLM_Q4_K 12
@@ -186,6 +186,37 @@ int dllm_qgemm_bias(int qtype, const void *w, int64_t N, int64_t K,
                     const void *x_q8k, const float *x_dmax, int64_t M,
                     const float *bias, float *y, int64_t ldy, void *workspace,
                     int64_t workspace_bytes, void *stream);
+
+/*
+ * Two GEMMs of one activation matrix in one launch: y_a = X_hat W_a^T (+ bias_a)
+ * and y_b = X_hat W_b^T (+ bias_b), e.g. a layer's Q + K projection (Q4_K)
+ * and its V projection (Q6_K), which read the same normalized hidden state
+ * (Development plan, "Compute design": every linear layer multiplies the L
+ * Q8_K activation rows by the layer's weight rows).  Each output is the
+ * same, bit for bit, as dllm_qgemm_bias on its own with a workspace of at
+ * least dllm_qgemm_workspace_bytes bytes, when this call's workspace has
+ * dllm_qgemm_pair_workspace_bytes(qtype_a, N_a, qtype_b, N_b, K, M) bytes
+ * (16-byte aligned; zero-filled once before first use, as dllm_qgemm's; with
+ * less, or NULL, both run without a K split, as dllm_qgemm without one).
+ * Where the two calls' tile plans have a grouped kernel (Q4_K tiles of 80
+ * tokens with Q6_K tiles, at 129..160 tokens for the step's shapes), their
+ * work-groups share one grid, so that each CU holds a tile of each; other
+ * plans run as the two launches in order on the stream.
+ *   qtype_*, w_*, N_*, bias_* (NULL: none), y_*, ldy_*   as for dllm_qgemm_bias
+ *   K, x_q8k, x_dmax, M   shared, as for dllm_qgemm
+ * y_a and y_b must not overlap each other, the workspace or the inputs.
+ * Argument errors are dllm_qgemm_bias's, checked for both before anything
+ * is enqueued.  dllm_qgemm_pair_workspace_bytes returns -1 for invalid
+ * arguments and 0 where neither GEMM splits K.
+ */
+int64_t dllm_qgemm_pair_workspace_bytes(int qtype_a, int64_t N_a, int qtype_b,
+                                        int64_t N_b, int64_t K, int64_t M);
+int dllm_qgemm_pair(int qtype_a, const void *w_a, int64_t N_a,
+                    const float *bias_a, float *y_a, int64_t ldy_a,
+                    int qtype_b, const void *w_b, int64_t N_b,
+                    const float *bias_b, float *y_b, int64_t ldy_b, int64_t K,
+                    const void *x_q8k, const float *x_dmax, int64_t M,
+                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * dllm_qgemm_bias for callers that cannot allocate device memory (code under

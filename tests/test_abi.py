@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_header_function(dl):
     names = _header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     lib = ctypes.CDLL(dl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -232,3 +232,25 @@ def test_no_environment_reads_in_the_library():
     for name in os.listdir(csrc):
         if name.endswith((".hip", ".hpp", ".h", ".cpp")):
             assert "getenv" not in open(os.path.join(csrc, name)).read(), name
+
+
+def test_pair_checks_both_gemms_before_launching(dl):
+    """dllm_qgemm_pair reports an error in either GEMM's arguments (or the
+    shared ones) before anything is enqueued; its workspace query rejects
+    invalid shapes with -1."""
+    L = dl.lib
+    ok = (dl.Q4_K, FAKE, 64, None, FAKE, 64)
+    assert L.dllm_qgemm_pair(*ok, 13, FAKE, 64, None, FAKE, 64, 256, FAKE, None, 1, None, 0, None) == dl.E_UNSUPPORTED
+    assert L.dllm_qgemm_pair(8, FAKE, 64, None, FAKE, 64, *ok, 256, FAKE, None, 1, None, 0, None) == dl.E_UNSUPPORTED
+    assert L.dllm_qgemm_pair(*ok, dl.Q6_K, FAKE, 64, None, None, 64, 256, FAKE, None, 1, None, 0, None) == dl.E_ARG
+    assert L.dllm_qgemm_pair(*ok, dl.Q6_K, None, 64, None, FAKE, 64, 256, FAKE, None, 1, None, 0, None) == dl.E_ARG
+    assert L.dllm_qgemm_pair(dl.Q4_K, FAKE, 64, None, FAKE, 63, dl.Q6_K, FAKE, 64, None, FAKE, 64, 256, FAKE, None, 1,
+                             None, 0, None) == dl.E_ARG
+    assert L.dllm_qgemm_pair(*ok, dl.Q6_K, FAKE, 0, None, FAKE, 64, 256, FAKE, None, 1, None, 0, None) == dl.E_SHAPE
+    assert L.dllm_qgemm_pair(*ok, dl.Q6_K, FAKE, 64, None, FAKE, 64, 300, FAKE, None, 1, None, 0, None) == dl.E_SHAPE
+    two = ctypes.c_void_p((1 << 20) + 2)
+    assert L.dllm_qgemm_pair(*ok, dl.Q6_K, FAKE, 64, two, FAKE, 64, 256, FAKE, None, 1, None, 0, None) == dl.E_ALIGN
+    assert dl.qgemm_pair_workspace_bytes(dl.Q4_K, 64, dl.Q6_K, 64, 300, 1) == -1
+    assert dl.qgemm_pair_workspace_bytes(dl.Q4_K, 64, 8, 64, 256, 1) == -1
+    assert dl.qgemm_pair_workspace_bytes(dl.Q4_K, 8192, dl.Q6_K, 4096, 4096, 148) == (
+        dl.qgemm_workspace_bytes(dl.Q6_K, 4096, 4096, 148))  # only V splits: its slices after the counters
