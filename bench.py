@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--profile-dominant", action="store_true",
                     help="for hardware-counter runs: a 256 MiB device copy (the counters' calibration), then "
                          "--steps launches of the step's dominant GEMM (one layer's gate/up), then exit")
-    ap.add_argument("--profile-kernel", choices=("lmhead", "attention", "rmsnorm", "swiglu") + tuple(STEP_CALLS),
+    ap.add_argument("--profile-kernel", choices=("lmhead", "attention", "rmsnorm", "swiglu", "pair") + tuple(STEP_CALLS),
                     default=None,
                     help="for hardware-counter runs: the same calibration copy, then --steps launches of one call of "
                          "the step as the step makes it (" + ", ".join(f"{k}: {v[3]}" for k, v in STEP_CALLS.items()) +
@@ -85,6 +85,7 @@ PMC_PASSES = {
 PMC_TARGETS = {
     "gateup": "qgemm_q4k_24576x4096_L148", "o": "qgemm_q4k_4096x4096_L148", "down6": "qgemm_q6k_4096x12288_L148",
     "v6": "qgemm_q6k_4096x4096_L148", "quant4096": "quantize_q8k_148x4096", "lmhead": "lmhead_q6k_126464x4096_rows32",
+    "pair": "qgemm_pair_q4k8192_q6k4096x4096_L148",
 }
 CUS, SIMDS, XCDS = 256, 4, 8  # MI355X
 
@@ -260,6 +261,20 @@ def profile_kernel(args):
             ws = dl.qgemm_workspace(q, N, K, L, dev)
             fn = lambda: dl.qgemm(q, w, N, K, xq, L, y=y, workspace=ws, x_dmax=dm)
         what = f"{what}, L={L}"
+    elif args.profile_kernel == "pair":
+        # an even layer's Q + K (Q4_K) and V (Q6_K) projections, one launch
+        x = synth.normal_f32((L, D), args.seed, f"prof-x-{D}", dev)
+        xq = torch.empty((L, D // 256 * 292), dtype=torch.uint8, device=dev)
+        dm = torch.empty(L, dtype=torch.float32, device=dev)
+        dl.quantize_q8k(x, xq, dm)
+        wa = synth.q4k_rows(2 * D, D, args.seed, f"prof-w-12-{2 * D}-{D}", dev)
+        wb = synth.q6k_rows(D, D, args.seed, f"prof-w-14-{D}-{D}", dev)
+        y = torch.empty((L, 3 * D), dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(256, dl.qgemm_pair_workspace_bytes(dl.Q4_K, 2 * D, dl.Q6_K, D, D, L)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: dl.qgemm_pair((dl.Q4_K, wa, 2 * D, y[:, :2 * D], None), (dl.Q6_K, wb, D, y[:, 2 * D:], None), D,
+                                   xq, L, workspace=ws, x_dmax=dm)
+        what = f"qgemm_pair Q+K Q4_K {2 * D}x{D} with V Q6_K {D}x{D}, L={L}"
     elif args.profile_kernel == "lmhead":
         w = synth.q6k_rows(VOCAB, D, args.seed, "output", dev)
         hidden = synth.normal_f32((L, D), args.seed, "hidden", dev)
@@ -791,8 +806,12 @@ def summarize_pmc(spec):
             d[r["Counter_Name"]] = float(r["Counter_Value"])
             d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             kname = r["Kernel_Name"]
-        for d in per.values():
-            for k, v in d.items():
+        # the first dispatch of a pass is left out: its counter window also
+        # holds the code object's first load (GRBM_GUI_ACTIVE several times
+        # the kernel's own)
+        ids = sorted(per)
+        for i in (ids[1:] if len(ids) > 1 else ids):
+            for k, v in per[i].items():
                 vals.setdefault(k, []).append(v)
     m = {k: sum(v) / len(v) for k, v in vals.items()}
     n_disp = len(vals["SQ_WAVES"])
@@ -819,7 +838,7 @@ def summarize_pmc(spec):
         lines.append(f"#   rocprofv3 --pmc {cs} --output-format csv -d {prefix}_{p} -o run -- "
                      f"python3 bench.py --profile-kernel {target} --steps 5")
     lines.append(f"#   python3 bench.py --summarize-pmc {target} {prefix}")
-    lines.append(f"# {n_disp} dispatches of the kernel over the passes, averaged")
+    lines.append(f"# {n_disp} dispatches of the kernel over the passes (each pass's first left out), averaged")
     lines.append("# mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs)")
     lines.append("# valu_per_mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA; valu_active, mfma_valu_coexec, wait_any,"
                  " wait_inst_any = SQ_ACTIVE_INST_VALU, SQ_VALU_MFMA_COEXEC_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY"
@@ -900,6 +919,8 @@ def summarize_traffic(target, prefix, out):
         "swiglu": (f"SwiGLU -> Q8_K, {L} x 2 x {FFN}", L * 2 * FFN * 4 + L * FFN // 256 * 292 + L * 4),
         "attention": (f"bidirectional attention, L={L}, 32 heads x 128 (f32 Q+K+V rows in, f32 out)",
                       L * 3 * D * 4 + L * D * 4),
+        "pair": (f"Q+K Q4_K {2 * D}x{D} with V Q6_K {D}x{D} in one launch",
+                 2 * D * D // 256 * 144 + D * D // 256 * 210 + L * D // 256 * 292 + L * 3 * D * 4),
     }
     if target == "dominant":
         q, N, K, what = 12, 2 * FFN, D, "gate+up Q4_K 24576x4096"
