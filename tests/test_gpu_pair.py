@@ -93,3 +93,40 @@ def test_pair_row_strided_outputs_into_one_buffer(dl):
         ref = oracle.gemm(q, w.cpu().numpy(), N, K, xqh[toks], len(toks))
         assert_close_rows(got[toks, c0:c0 + N], ref, f"pair {q}:{N} vs oracle")
 
+
+
+def test_pair_graph_replays_match_eager(dl):
+    """quantize -> the grouped Q + K / V call (V with its K split over the
+    pair's workspace), captured once in a HIP graph and replayed four times
+    with unrelated eager work between the replays: every replay gives the
+    eager bits."""
+    qa, Na, qb, Nb, K, M = 12, 8192, 14, 4096, 4096, 148
+    wa, wb, xq, dm, _, _ = _operands(dl, qa, Na, qb, Nb, K, M, False, 93)
+    x = synth.normal_f32((M, K), 93, "pair-graph-x", DEV)
+    y = torch.empty((M, Na + Nb), dtype=torch.float32, device=DEV)
+    nb = dl.qgemm_pair_workspace_bytes(qa, Na, qb, Nb, K, M)
+    assert nb > 0, "V must take its K split at this shape"
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+
+    def run():
+        dl.quantize_q8k(x, xq, dm)
+        dl.qgemm_pair((qa, wa, Na, y[:, :Na], None), (qb, wb, Nb, y[:, Na:], None), K, xq, M, workspace=ws, x_dmax=dm)
+
+    run()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.current_stream().wait_stream(st)
+    for k in range(4):
+        y.zero_()
+        junk = torch.randn(1 << 20, device=DEV) * 3.0
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {k} differs from the eager run"
+        del junk
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0, "split counters not reset"
