@@ -55,6 +55,8 @@ CASES = [
     (12, 4096, 14, 512, 3584, 148, True),     # Dream-7B: Q + K with V, both with bias (grouped)
     (12, 8192, 14, 4096, 4096, 37, False),    # a small canvas: no grouped kernel, two launches
     (12, 333, 14, 100, 1024, 150, True),      # ragged rows, planner-chosen plans
+    (12, 2048, 12, 1024, 2048, 148, False),   # two Q4_K GEMMs: no grouped kernel, two launches
+    (14, 300, 12, 500, 512, 1, True),         # one token
 ]
 
 
