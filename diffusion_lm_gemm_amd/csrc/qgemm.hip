@@ -30,9 +30,12 @@
 // staged in LDS and shared by the waves; each wave unpacks only its own rows.
 // The weight side of the minimum term, -dmin * m, is exact as two f16 halves
 // for every f16 dmin up to 65504/63 (a 6-bit m times an 11-bit significand
-// whose lowest bit is at least 2^-24, subnormals included).  K may be split across work-groups (grid.y): each writes its
-// partial tile to a workspace slice, and the last of a tile's work-groups to
-// finish sums the slices in split order (no second kernel).
+// whose lowest bit is at least 2^-24, subnormals included).  K may be split
+// across work-groups (grid.y): each writes its partial tile to a workspace
+// slice, and the last of a tile's work-groups to finish sums the slices in
+// split order (no second kernel).  One work-group's work is the device
+// function qgemm_wg; k_qgemm runs it on its own grid, and k_qgemm_pair runs
+// two GEMMs of the same activations (two four-wave plans) in one grid.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "unpack.hpp"
