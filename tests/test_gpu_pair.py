@@ -57,6 +57,11 @@ CASES = [
     (12, 333, 14, 100, 1024, 150, True),      # ragged rows, planner-chosen plans
     (12, 2048, 12, 1024, 2048, 148, False),   # two Q4_K GEMMs: no grouped kernel, two launches
     (14, 300, 12, 500, 512, 1, True),         # one token
+    # planner-chosen grouped plans whose grids are not whole groups of eight
+    # and differ in size: A 132 work-groups (16.5 groups) with B 64; A 88
+    # with B 128 (the larger grid's groups run after the alternation)
+    (12, 2112, 14, 1000, 1024, 150, True),
+    (12, 704, 14, 4096, 1024, 150, False),
 ]
 
 
