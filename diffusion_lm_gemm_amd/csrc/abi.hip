@@ -153,7 +153,7 @@ constexpr Tuned kTuned[] = {
     {12, 12288, 4096, 129, 160, 7, 2},  // Q + K + V
     {12, 8192, 4096, 129, 160, 6, 1},   // Q + K (V in Q6_K)
     {12, 4096, 4096, 129, 160, 6, 4},   // O
-    {14, 4096, 4096, 129, 160, 5, 4},   // V
+    {14, 4096, 4096, 129, 160, 6, 2},   // V (run with Q + K in one launch; alone, (5, 4) is faster)
     {12, 4096, 12288, 129, 160, 6, 4},  // down
     {14, 4096, 12288, 129, 160, 5, 8},  // down
     // Dream-7B (hidden 3584, 4 key/value heads of 128, FFN 18944)
